@@ -1,0 +1,24 @@
+"""fp64 CPU oracle for the TACO FP8 compression operator.
+
+Test infrastructure only: see ``oracle/taco_oracle.py`` for what it computes and
+which passages it follows.  Product code never imports this package.
+"""
+from .taco_oracle import (  # noqa: F401
+    Q_MAX,
+    ash_scale,
+    bf16_bits_to_f64,
+    block_energy,
+    compress,
+    decompress,
+    decompress_f64,
+    decompress_sum,
+    ds_scale,
+    e4m3_decode,
+    e4m3_decode_code,
+    e4m3_encode,
+    e4m3_table,
+    f64_to_bf16_bits,
+    hadamard,
+    hadamard_rotate,
+    quantize,
+)

@@ -1,0 +1,257 @@
+"""Plain fp64 CPU oracle for the TACO FP8 compression operator.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import or call this module.  It
+shares no code, table or helper with the HIP library in
+``fp8_compression_tensor_taco_amd/``; the only thing both sides consume is the
+seeded input generator, which holds none of the method's arithmetic.
+
+Sources.  Citations name the page and the section on it:
+
+* "TACO pt-summary" -- the Portuguese structured summary on gist.science of
+  *TACO: Efficient Communication Compression of Intermediate Tensors for Scalable
+  Tensor-Parallel LLM Training* (arXiv 2604.24088).  Its section 2.A ("Por que
+  FP8?"), 2.B.1 (ASH), 2.B.2 (DS) and 2.B.3 (kernel fusion and overlap) describe
+  the operator.
+* "TACO de-explainer" -- the German explainer of the same paper on gist.science,
+  sections 2 (ASH) and 3 (Dual-Scale).
+* "TACO zh-news" -- the Chinese euno.news summary, section "方法论" (method).
+
+What the method computes.  Where the pages leave a step open, the plainest
+reading the rest supports is taken and marked "reading" below:
+
+1. x is a bf16 tensor [T, H]; blocks are B consecutive elements of a row
+   (reading: the pages give no block shape or size; B is a power of two that
+   divides H).  bf16 is widened to fp64 exactly.
+2. Block energy m_k = (1/B) * sum_i x_i^2, the raw (not mean-subtracted) second
+   moment [TACO pt-summary, 2.B.1; its section 2.B.3 says "variance" for the
+   same quantity, read as the raw moment named in 2.B.1].
+3. ASH scale alpha_k = fp32(sqrt(E / m_k)), or 1 for an all-zero block
+   (reading: the zero case and the fp32 storage are not on the pages); it
+   normalises the block energy to the target E before the rotation
+   [TACO pt-summary, 2.B.1 and 2.B.2 (pre-rotation scale)].  The stored fp32
+   value is the one used afterwards.
+4. Orthonormal Sylvester-Hadamard rotation y_k = alpha_k * H_B x_k / sqrt(B)
+   [TACO pt-summary, 2.B.1 (orthogonal Hadamard rotation, energy preserving)].
+   Reading: natural (Sylvester) order, no random sign flips.
+5. DS post-rotation scale s = fp32(448 / max|y|) over the whole tensor (1 if the
+   tensor is zero), which makes every rotated value fit the FP8 range
+   [TACO pt-summary, 2.B.2 (post-rotation scale, Q_max)].  Reading: the page
+   speaks of two scalars per block; a post-rotation scale that mapped each
+   block's own maximum to Q_max would cancel alpha_k exactly and make ASH a
+   no-op on the codes, so s is one scalar per tensor (the per-tensor scale of
+   TACO zh-news, method section), while alpha_k stays per block.
+6. Codes q = E4M3FN(s * y), round to nearest, ties to even, saturating at +-448
+   [TACO pt-summary, 2.A (E4M3) and 2.B.2].  Reading: OCP E4M3FN (bias 7,
+   Q_max 448); rounding mode and saturation are not on the pages.
+7. Decompression undoes both scales and the rotation, rounding once to bf16
+   [TACO pt-summary, 2.B.2 (reconstruction uses both scales)].
+8. Decompress-and-sum is the local reduction step of the two-shot all-reduce:
+   each part is decompressed with its own scales, the parts are summed in
+   fp64 and the sum is rounded once [TACO pt-summary, 2.B.3].  Reading: the
+   pages name the two-shot scheme but not its local step's arithmetic.
+
+Arithmetic is fp64 throughout; the only roundings are at the storage points the
+method defines (alpha and s to fp32, codes to E4M3, outputs to bf16).  Dense
+matrix products (numpy matmul) serve as the Hadamard step; nothing is blocked,
+fused or reordered beyond that.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+Q_MAX = 448.0  # largest finite E4M3FN magnitude [TACO pt-summary, 2.B.2: Q_max]
+
+
+# ---------------------------------------------------------------------------
+# E4M3FN (OCP 8-bit float, 1 sign / 4 exponent / 3 mantissa bits, bias 7,
+# no infinities, NaN = S.1111.111).  The pages name the format [TACO
+# pt-summary, 2.A]; its bit layout is the OCP OFP8 definition.
+# ---------------------------------------------------------------------------
+
+def e4m3_decode_code(code: int) -> float:
+    """Value of one E4M3FN code, straight from the bit-field definition."""
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return float("nan")
+    if exp == 0:                       # subnormal: man/8 * 2^(1-7)
+        return sign * (man / 8.0) * 2.0 ** -6
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+def e4m3_table() -> np.ndarray:
+    """fp64 value of every code 0..255 (NaN for 0x7F and 0xFF)."""
+    return np.array([e4m3_decode_code(c) for c in range(256)], dtype=np.float64)
+
+
+_TABLE = e4m3_table()
+# Non-negative finite codes 0x00..0x7E in code order are strictly increasing.
+_POS = _TABLE[:0x7F].copy()
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of each code."""
+    return _TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Nearest E4M3FN code to each fp64 value; ties go to the even code;
+    magnitudes beyond 448 saturate to 448.  The sign bit follows the sign of v
+    (so a negative value that rounds to zero gives 0x80).  Input must be finite.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    if not np.all(np.isfinite(v)):
+        raise ValueError("e4m3_encode: non-finite input")
+    mag = np.abs(v)
+    # lo = largest code whose value is <= mag (code order == value order)
+    lo = np.searchsorted(_POS, mag, side="right") - 1
+    lo = np.clip(lo, 0, 0x7E)
+    hi = np.minimum(lo + 1, 0x7E)
+    d_lo = mag - _POS[lo]
+    d_hi = _POS[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (lo % 2 == 1))
+    pick_hi &= hi != lo                # at 448 there is nothing above: saturate
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code |= np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+    return code
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 (1 sign / 8 exponent / 7 mantissa bits), handled as uint16 patterns.
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact widening: a bf16 pattern is the top half of an fp32 pattern."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):              # NaN patterns stay NaN
+        return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """One rounding, fp64 -> bf16, to nearest with ties to even.
+
+    A finite bf16 value is k * 2^(e-8) with 128 <= k < 256 for |v| in
+    [2^(e-1), 2^e) (normal range), or k * 2^-133 below 2^-126 (subnormals).
+    Magnitudes that round past the largest finite value become infinity.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)                                   # |v| in [2^(e-1), 2^e)
+    quantum = np.ldexp(1.0, np.maximum(e - 8, -133))
+    r = np.rint(v / quantum) * quantum                   # rint: ties to even
+    with np.errstate(over="ignore"):
+        r32 = r.astype(np.float32)                       # exact: r is a bf16 value
+    return (r32.view(np.uint32) >> 16).astype(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Sylvester-Hadamard matrix [TACO pt-summary, 2.B.1: orthogonal Hadamard rotation]
+# ---------------------------------------------------------------------------
+
+def hadamard(n: int) -> np.ndarray:
+    """H_n[i, j] = (-1)^popcount(i & j), natural (Sylvester) order, entries +-1."""
+    if n < 1 or n & (n - 1):
+        raise ValueError("Hadamard order must be a power of two")
+    i = np.arange(n)
+    parity = np.zeros((n, n), dtype=np.int64)
+    anded = i[:, None] & i[None, :]
+    while np.any(anded):
+        parity ^= anded & 1
+        anded = anded >> 1
+    return np.where(parity == 1, -1.0, 1.0)
+
+
+# ---------------------------------------------------------------------------
+# Steps of the compress side, one function per step
+# ---------------------------------------------------------------------------
+
+def _check_shape(tokens: int, hidden: int, block: int) -> None:
+    if block < 1 or block & (block - 1):
+        raise ValueError("block must be a power of two")
+    if tokens < 1 or hidden < 1 or hidden % block:
+        raise ValueError("hidden must be a positive multiple of block")
+
+
+def block_energy(xb: np.ndarray) -> np.ndarray:
+    """m_k: mean of squares of each block (rows of xb) [TACO pt-summary, 2.B.1]."""
+    return np.sum(xb * xb, axis=1) / xb.shape[1]
+
+
+def ash_scale(m: np.ndarray, target_energy: float) -> np.ndarray:
+    """alpha_k = fp32(sqrt(E / m_k)); 1 where m_k == 0 [TACO pt-summary, 2.B.1, 2.B.2]."""
+    safe = np.where(m > 0, m, 1.0)
+    alpha = np.where(m > 0, np.sqrt(np.float64(target_energy) / safe), 1.0)
+    return alpha.astype(np.float32)
+
+
+def hadamard_rotate(xb: np.ndarray, alpha: np.ndarray) -> np.ndarray:
+    """y_k = alpha_k * H_B x_k / sqrt(B) [TACO pt-summary, 2.B.1]."""
+    B = xb.shape[1]
+    hx = xb @ hadamard(B).T                      # row k holds (H_B x_k)^T
+    a = np.asarray(alpha, dtype=np.float32).astype(np.float64).reshape(-1)
+    return a[:, None] * hx / np.sqrt(np.float64(B))
+
+
+def ds_scale(y: np.ndarray) -> np.float32:
+    """s = fp32(Q_max / max|y|); 1 for an all-zero tensor [TACO pt-summary, 2.B.2]."""
+    amax = float(np.max(np.abs(y))) if y.size else 0.0
+    return np.float32(Q_MAX / amax) if amax > 0 else np.float32(1.0)
+
+
+def quantize(y: np.ndarray, s: np.float32) -> np.ndarray:
+    """q = E4M3FN_RNE_sat(s * y), product in fp64 [TACO pt-summary, 2.A, 2.B.2]."""
+    return e4m3_encode(np.float64(s) * y)
+
+
+def compress(x_bits: np.ndarray, block: int, target_energy: float = 1.0):
+    """Compress a bf16 tensor given as uint16 patterns of shape [T, H].
+
+    Returns (q uint8 [T, H], alpha float32 [T, H/block], s float32).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, H = x_bits.shape
+    _check_shape(T, H, block)
+    E = float(np.float32(target_energy))
+    if not (np.isfinite(E) and E > 0):
+        raise ValueError("target energy must be finite and > 0")
+    xb = bf16_bits_to_f64(x_bits).reshape(-1, block)
+    alpha = ash_scale(block_energy(xb), E)
+    y = hadamard_rotate(xb, alpha)
+    s = ds_scale(y)
+    q = quantize(y, s)
+    return q.reshape(T, H), alpha.reshape(T, H // block), s
+
+
+# ---------------------------------------------------------------------------
+# Decompress side [TACO pt-summary, 2.B.2 (reconstruction), 2.B.3 (two-shot)]
+# ---------------------------------------------------------------------------
+
+def decompress_f64(q: np.ndarray, alpha: np.ndarray, s, block: int) -> np.ndarray:
+    """Unrounded reconstruction (1/alpha_k) * H_B (dec(q_k) / s) / sqrt(B), fp64 [T, H]."""
+    q = np.asarray(q, dtype=np.uint8)
+    T, H = q.shape
+    _check_shape(T, H, block)
+    d = e4m3_decode(q).reshape(-1, block) / np.float64(np.float32(s))
+    h = d @ hadamard(block).T / np.sqrt(np.float64(block))
+    a = np.asarray(alpha, dtype=np.float32).astype(np.float64).reshape(-1)
+    return (h / a[:, None]).reshape(T, H)
+
+
+def decompress(q: np.ndarray, alpha: np.ndarray, s, block: int) -> np.ndarray:
+    """bf16 reconstruction as uint16 patterns [T, H], one rounding from fp64."""
+    return f64_to_bf16_bits(decompress_f64(q, alpha, s, block))
+
+
+def decompress_sum(parts, block: int) -> np.ndarray:
+    """Sum over parts p of the unrounded reconstruction of (q_p, alpha_p, s_p),
+    in fp64, rounded once to bf16 (uint16 patterns).  Literal order:
+    dequantise, inverse rotation, unscale, then sum."""
+    parts = list(parts)
+    if not parts:
+        raise ValueError("decompress_sum needs at least one part")
+    acc = None
+    for q, alpha, s in parts:
+        r = decompress_f64(q, alpha, s, block)
+        acc = r if acc is None else acc + r
+    return f64_to_bf16_bits(acc)
