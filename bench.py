@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Throughput of the TACO FP8 compression operator on one MI355X.
+
+One step is one pass of the whole hot path on the GPT-3-6.7B-shaped TP layer
+(bf16 [4096, 4096], block 128), i.e. what one GPU does per layer:
+  compress(forward activation) -> decompress,
+  compress(backward gradient)  -> decompress,
+  decompress_sum(4 compressed partial sums of the same shape)
+(the 4 partial sums stand for the peers' contributions; they are compressed
+once before timing, as the peers would do on their own GPUs).
+
+Inputs are resident in HBM when timing starts.  To keep the timed traffic in
+HBM rather than the 256 MB Infinity Cache, the step rotates over R complete
+buffer sets (>= 1 GiB together).  `value` is bf16 bytes moved by the calls
+(bf16 in for compress, bf16 out for the decompressions) per second.
+
+Each step is launched as one HIP graph (captured per buffer set), so the timed
+region measures the GPU rather than the host's per-call enqueue cost.  The
+per-op durations (and the roofline of the compress kernels) come from their own
+timed regions: graphs of back-to-back calls of one op over every buffer set.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compress/decompress GB/s (bf16 in) and % of MI355X HBM peak, 1 GPU"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+WORKLOAD = "gpt3_6p7b"
+TOKENS, HIDDEN, BLOCK, NPARTS = 4096, 4096, 128, 4
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "compress_gpt3_6p7b_counters.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--rotate", type=int, default=4, help="buffer sets rotated over (>= 1 GiB total)")
+    p.add_argument("--cpu-rows", type=int, default=1024,
+                   help="rows of the workload the oracle is timed on (cpu_baseline)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--engine", choices=["auto", "valu", "mfma"], default=None,
+                   help="rotation engine of compress (default: the library's choice)")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "fp8_compression_tensor_taco_amd", "csrc", "taco.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per compress call from the committed rocprofv3 counter run,
+    or None if the kernel source changed since the counters were taken."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return c.get("traffic_bytes_per_call")
+
+
+def cpu_baseline(rows: int):
+    """The oracle, as it is, on the first `rows` rows of the same step (1 thread)."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from fp8_compression_tensor_taco_amd import workloads as W
+
+    act = W.bf16_bits(W.make("gpt3_6p7b_act", seed=0, tokens=rows))
+    grad = W.bf16_bits(W.make("gpt3_6p7b_grad", seed=1, tokens=rows))
+    parts = [oracle.compress(W.bf16_bits(W.make("gpt3_6p7b_act", seed=10 + p, tokens=rows)), BLOCK)
+             for p in range(NPARTS)]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for x in (act, grad):
+            q, a, s = oracle.compress(x, BLOCK)
+            oracle.decompress(q, a, s, BLOCK)
+        oracle.decompress_sum(parts, BLOCK)
+        dt = time.perf_counter() - t0
+    nbytes = 2 * rows * HIDDEN * 5          # bf16 bytes of the 5 calls
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one step on rows 0..{rows - 1} of the [{TOKENS},{HIDDEN}] workload "
+                      f"({rows}x{HIDDEN} per tensor), numpy fp64, BLAS limited to 1 thread, "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the operator needs no collectives and this build "
+              f"has no multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE={world}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp8_compression_tensor_taco_amd as taco
+    from fp8_compression_tensor_taco_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    taco.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- resident inputs, R rotating buffer sets
+    act = W.make("gpt3_6p7b_act", seed=0).to(dev)
+    grad = W.make("gpt3_6p7b_grad", seed=1).to(dev)
+    part_src = [taco.compress(W.make("gpt3_6p7b_act", seed=10 + p).to(dev), BLOCK)
+                for p in range(NPARTS)]
+    torch.cuda.synchronize()
+    nscales = TOKENS * HIDDEN // BLOCK
+    sets = []
+    for _ in range(args.rotate):
+        s = {
+            "act": act.clone(), "grad": grad.clone(),
+            "parts": [tuple(t.clone() for t in p) for p in part_src],
+            "q": [torch.empty((TOKENS, HIDDEN), dtype=torch.uint8, device=dev) for _ in range(2)],
+            "a": [torch.empty((TOKENS, HIDDEN // BLOCK), dtype=torch.float32, device=dev) for _ in range(2)],
+            "s": [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(2)],
+            "xh": [torch.empty((TOKENS, HIDDEN), dtype=torch.bfloat16, device=dev) for _ in range(2)],
+            "sum": torch.empty((TOKENS, HIDDEN), dtype=torch.bfloat16, device=dev),
+        }
+        sets.append(s)
+    del act, grad, part_src
+    ws = torch.zeros(taco.workspace_bytes(TOKENS, HIDDEN, BLOCK), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    if args.engine:
+        taco.set_rotation_engine(args.engine)
+    set_bytes = sum(t.numel() * t.element_size() for t in
+                    [sets[0]["act"], sets[0]["grad"], *sets[0]["q"], *sets[0]["a"], *sets[0]["xh"],
+                     sets[0]["sum"], *[t for p in sets[0]["parts"] for t in p]])
+
+    ops = ["compress", "decompress", "decompress_sum"]
+
+    def op_compress(st, k):
+        x = st["act"] if k == 0 else st["grad"]
+        taco.compress(x, BLOCK, q=st["q"][k], alpha=st["a"][k], scale=st["s"][k], workspace=ws)
+
+    def op_decompress(st, k):
+        taco.decompress(st["q"][k], st["a"][k], st["s"][k], BLOCK, out=st["xh"][k])
+
+    def op_sum(st):
+        taco.decompress_sum(st["parts"], BLOCK, out=st["sum"])
+
+    def step(st):
+        for k in range(2):
+            op_compress(st, k)
+            op_decompress(st, k)
+        op_sum(st)
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    # ---- HIP graphs: one per buffer set for the step, and one per op that runs
+    # that op back to back over every set (so its inputs cycle through >1 GiB)
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    step_graphs = [capture(lambda st=st: step(st)) for st in sets]
+    op_graphs = {
+        "compress": (capture(lambda: [op_compress(st, k) for st in sets for k in range(2)]), 2 * len(sets)),
+        "decompress": (capture(lambda: [op_decompress(st, k) for st in sets for k in range(2)]), 2 * len(sets)),
+        "decompress_sum": (capture(lambda: [op_sum(st) for st in sets]), len(sets)),
+    }
+    for g in step_graphs:
+        g.replay()
+    for g, _ in op_graphs.values():
+        g.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps (graph replays) bracketed by events on the launch stream
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step_graphs[i % len(step_graphs)].replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # ---- per-op timed regions: average duration of one call of each op
+    reps = max(1, args.steps // 4)
+    avg_us = {}
+    for op in ops:
+        g, calls = op_graphs[op]
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg_us[op] = 1e3 * e0.elapsed_time(e1) / (reps * calls)
+
+    N = TOKENS * HIDDEN
+    bf16_bytes_step = 2 * N * 5
+    value = bf16_bytes_step / (ms_step / 1e3) / 1e9
+    alg = {
+        "compress": 2 * N + N + 4 * nscales + 4,
+        "decompress": N + 4 * nscales + 4 + 2 * N,
+        "decompress_sum": NPARTS * (N + 4 * nscales + 4) + 2 * N,
+    }
+    achieved = alg["compress"] / (avg_us["compress"] * 1e-6) / 1e9
+    traffic = measured_traffic()
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "GPT-3-6.7B-shaped TP layer, bf16 [4096, 4096], block 128, target energy 1.0: "
+                        "compress+decompress of the forward activation and of the backward gradient, "
+                        "plus decompress_sum of 4 compressed partial sums",
+            "tokens": TOKENS, "hidden": HIDDEN, "block": BLOCK, "decompress_sum_parts": NPARTS,
+            "rotating_buffer_sets": args.rotate,
+            "rotating_bytes": set_bytes * args.rotate,
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "kernel": "compress (statistics + quantisation kernels, " + taco.get_rotation_engine() + " rotation)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes": alg["compress"],
+            "avg_us": round(avg_us["compress"], 3),
+        },
+        "ops": {
+            op: {"avg_us": round(avg_us[op], 3),
+                 "bf16_GBps": round(2 * N / (avg_us[op] * 1e-6) / 1e9, 1),
+                 "algorithmic_GBps": round(alg[op] / (avg_us[op] * 1e-6) / 1e9, 1),
+                 "hbm_frac": round(alg[op] / (avg_us[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            for op in ops
+        },
+        "wall_s_timed": round(t_wall, 4),
+        "timing": "step = one HIP-graph replay of the 5 calls; per-op figures from graphs of back-to-back "
+                  "calls over all buffer sets",
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

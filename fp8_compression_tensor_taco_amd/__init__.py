@@ -1,1 +1,25 @@
-"""MI355X-native TACO FP8 compression operator (placeholder; binding added with the library)."""
+"""MI355X-native TACO FP8 compression operator for tensor-parallel intermediate tensors.
+
+Python face of libtaco (include/taco.h): ``compress``, ``decompress`` and
+``decompress_sum`` over bf16 [tokens, hidden] GPU tensors.  The library is
+loaded on first use and the calls raise if it is missing; there is no CPU path.
+"""
+from ._binding import (  # noqa: F401
+    TACO_MAX_PARTS,
+    TacoError,
+    compress,
+    get_rotation_engine,
+    set_rotation_engine,
+    decompress,
+    decompress_sum,
+    library_path,
+    load,
+    num_scales,
+    version,
+    workspace_bytes,
+)
+
+__all__ = [
+    "TACO_MAX_PARTS", "TacoError", "compress", "get_rotation_engine", "set_rotation_engine", "decompress", "decompress_sum",
+    "library_path", "load", "num_scales", "version", "workspace_bytes",
+]

@@ -1,0 +1,248 @@
+"""ctypes binding over libtaco's C ABI (include/taco.h).
+
+Argument marshalling only: every step of compress / decompress / decompress-sum
+runs in the HIP kernels of libtaco.so.  torch provides device memory and the
+current stream.  There is no CPU fallback: without the built library, or with
+tensors that are not on a GPU, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+from .build import LIB_PATH
+
+TACO_MAX_PARTS = 8
+_STATUS = {
+    0: "TACO_OK", 1: "TACO_ERR_NULL", 2: "TACO_ERR_ALIGN", 3: "TACO_ERR_SHAPE",
+    4: "TACO_ERR_UNSUPPORTED_BLOCK", 5: "TACO_ERR_BAD_ENERGY", 6: "TACO_ERR_WORKSPACE",
+    7: "TACO_ERR_BAD_NPARTS", 8: "TACO_ERR_HIP", 9: "TACO_ERR_BAD_ENGINE",
+}
+ENGINES = {"auto": 0, "valu": 1, "mfma": 2}
+
+
+class TacoError(RuntimeError):
+    """A libtaco call returned a nonzero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+        self.name = _STATUS.get(status, "TACO_ERR_UNKNOWN")
+
+
+_lib = None
+_lock = threading.Lock()
+_workspaces: dict[int, torch.Tensor] = {}
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libtaco.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"libtaco.so not found at {LIB_PATH}; build it first with "
+                "`python -m fp8_compression_tensor_taco_amd.build` (no CPU fallback exists)")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.taco_status_string.restype = ctypes.c_char_p
+        lib.taco_status_string.argtypes = [ctypes.c_int]
+        lib.taco_version.restype = ctypes.c_char_p
+        lib.taco_version.argtypes = []
+        lib.taco_set_rotation_engine.restype = ctypes.c_int
+        lib.taco_set_rotation_engine.argtypes = [ctypes.c_int]
+        lib.taco_get_rotation_engine.restype = ctypes.c_int
+        lib.taco_get_rotation_engine.argtypes = []
+        lib.taco_num_scales.restype = _i64
+        lib.taco_num_scales.argtypes = [_i64, _i64, _i32]
+        lib.taco_compress_workspace_bytes.restype = ctypes.c_size_t
+        lib.taco_compress_workspace_bytes.argtypes = [_i64, _i64, _i32]
+        lib.taco_compress.restype = ctypes.c_int
+        lib.taco_compress.argtypes = [_vp, _i64, _i64, _i32, ctypes.c_float, _vp, _vp, _vp,
+                                      _vp, ctypes.c_size_t, _vp]
+        lib.taco_decompress.restype = ctypes.c_int
+        lib.taco_decompress.argtypes = [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+        lib.taco_decompress_sum.restype = ctypes.c_int
+        lib.taco_decompress_sum.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                            ctypes.POINTER(_vp), _i32, _i64, _i64, _i32, _vp, _vp]
+        _lib = lib
+        return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load().taco_status_string(status).decode()
+        raise TacoError(status, msg)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _require_buffer(t: torch.Tensor, name: str, dtype, numel: int, shape=None) -> None:
+    """Output / input buffers must be contiguous, of the right dtype and size:
+    the kernels index them by the shape alone."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
+
+
+def _require_gpu(*tensors: torch.Tensor) -> torch.device:
+    dev = tensors[0].device
+    for t in tensors:
+        if t.device.type != "cuda":
+            raise ValueError("libtaco works on GPU tensors only (no CPU fallback)")
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def version() -> str:
+    return load().taco_version().decode()
+
+
+def set_rotation_engine(name: str) -> None:
+    """Rotation engine of compress for this process: "auto", "valu" or "mfma"."""
+    if name not in ENGINES:
+        raise ValueError(f"unknown engine {name!r}; expected one of {sorted(ENGINES)}")
+    _check(load().taco_set_rotation_engine(ENGINES[name]))
+
+
+def get_rotation_engine() -> str:
+    v = load().taco_get_rotation_engine()
+    return {i: n for n, i in ENGINES.items()}[v]
+
+
+def num_scales(tokens: int, hidden: int, block: int) -> int:
+    return int(load().taco_num_scales(tokens, hidden, block))
+
+
+def workspace_bytes(tokens: int, hidden: int, block: int) -> int:
+    return int(load().taco_compress_workspace_bytes(tokens, hidden, block))
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _workspaces.get(idx)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _workspaces[idx] = ws
+    return ws
+
+
+def compress(x: torch.Tensor, block: int, target_energy: float = 1.0, *,
+             q: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
+             scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+             stream=None):
+    """Compress a bf16 [tokens, hidden] GPU tensor.
+
+    Returns (q uint8 [tokens, hidden], alpha float32 [tokens, hidden/block],
+    scale float32 [1]).  Output tensors may be passed in to avoid allocation.
+    """
+    lib = load()
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    dev = _require_gpu(x)
+    x = x.contiguous()
+    T, H = x.shape
+    n = lib.taco_num_scales(T, H, block)
+    if n < 0:
+        _check(4 if block not in (64, 128, 256) else 3)
+    if q is None:
+        q = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    if alpha is None:
+        alpha = torch.empty((T, H // block), dtype=torch.float32, device=dev)
+    if scale is None:
+        scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    need = lib.taco_compress_workspace_bytes(T, H, block)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    _require_gpu(x, q, alpha, scale, workspace)
+    _require_buffer(q, "q", torch.uint8, T * H, (T, H))
+    _require_buffer(alpha, "alpha", torch.float32, n)
+    _require_buffer(scale, "scale", torch.float32, 1)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _check(lib.taco_compress(_ptr(x), T, H, block, float(target_energy), _ptr(q), _ptr(alpha),
+                             _ptr(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(dev, stream)))
+    return q, alpha, scale
+
+
+def decompress(q: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, block: int, *,
+               out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decompress (q, alpha, scale) into a bf16 [tokens, hidden] GPU tensor."""
+    lib = load()
+    if q.dim() != 2 or q.dtype != torch.uint8:
+        raise ValueError("q must be a 2-D uint8 tensor")
+    if alpha.dtype != torch.float32 or scale.dtype != torch.float32:
+        raise ValueError("alpha and scale must be float32")
+    dev = _require_gpu(q, alpha, scale)
+    T, H = q.shape
+    if alpha.numel() != max(lib.taco_num_scales(T, H, block), 0):
+        raise ValueError("alpha has the wrong number of elements for this shape and block")
+    if scale.numel() < 1:
+        raise ValueError("scale must hold one float32")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _require_gpu(q, out)
+    _require_buffer(out, "out", torch.bfloat16, T * H, (T, H))
+    _check(lib.taco_decompress(_ptr(q.contiguous()), _ptr(alpha.contiguous()), _ptr(scale), T, H,
+                               block, _ptr(out), _stream(dev, stream)))
+    return out
+
+
+def decompress_sum(parts, block: int, *, out: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """Sum of the decompressions of ``parts`` (a list of (q, alpha, scale)), rounded once to bf16."""
+    lib = load()
+    parts = [(q.contiguous(), a.contiguous(), s) for q, a, s in parts]
+    if not 1 <= len(parts) <= TACO_MAX_PARTS:
+        _check(7)
+    dev = _require_gpu(*[t for p in parts for t in p])
+    T, H = parts[0][0].shape
+    for q, a, s in parts:
+        if q.shape != (T, H) or q.dtype != torch.uint8:
+            raise ValueError("every part's q must be uint8 with the same shape")
+        if a.dtype != torch.float32 or s.dtype != torch.float32:
+            raise ValueError("alpha and scale must be float32")
+        if a.numel() != max(lib.taco_num_scales(T, H, block), 0):
+            raise ValueError("alpha has the wrong number of elements for this shape and block")
+        if s.numel() < 1:
+            raise ValueError("scale must hold one float32")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _require_gpu(parts[0][0], out)
+    _require_buffer(out, "out", torch.bfloat16, T * H, (T, H))
+    for q, _, _ in parts:
+        if q.data_ptr() == out.data_ptr():
+            raise ValueError("out may not alias an input")
+    P = len(parts)
+    qa = (_vp * P)(*[q.data_ptr() for q, _, _ in parts])
+    aa = (_vp * P)(*[a.data_ptr() for _, a, _ in parts])
+    sa = (_vp * P)(*[s.data_ptr() for _, _, s in parts])
+    _check(lib.taco_decompress_sum(qa, aa, sa, P, T, H, block, _ptr(out), _stream(dev, stream)))
+    return out

@@ -1,0 +1,145 @@
+/*
+ * libtaco -- TACO's fused FP8 compression operator for tensor-parallel
+ * intermediate tensors, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources.  "TACO pt-summary" is the Portuguese structured summary on
+ * gist.science of "TACO: Efficient Communication Compression of Intermediate
+ * Tensors for Scalable Tensor-Parallel LLM Training" (arXiv 2604.24088);
+ * "TACO zh-news" is the Chinese euno.news summary of the same paper.
+ *
+ * Data model (every call):
+ *   x      bf16 [tokens, hidden], row-major, contiguous.  N = tokens * hidden.
+ *   block  B in {64, 128, 256}; hidden % B == 0.  Block k is the B consecutive
+ *          elements [k*B, (k+1)*B) of the flattened tensor (always inside one row).
+ *   q      uint8 [tokens, hidden]: OCP FP8 E4M3FN codes (bias 7, max 448).
+ *   alpha  fp32 [tokens, hidden / B]: the per-block ASH scale.
+ *   scale  fp32 [1]: the per-tensor DS scale s.
+ * Compression computes, per block k,
+ *   m_k     = (1/B) sum_i x_i^2                       (raw second moment)
+ *   alpha_k = sqrt(E / m_k)      (1 if m_k == 0)      (ASH, to target energy E)
+ *   y_k     = alpha_k * H_B x_k / sqrt(B)              (orthonormal Sylvester-Hadamard)
+ * then s = 448 / max|y| over the whole tensor (1 if it is zero) and
+ *   q = E4M3FN(s * y), round to nearest even, saturating at +-448.
+ * Decompression returns bf16((1/alpha_k) * H_B (decode(q_k) / s) / sqrt(B)).
+ *
+ * Pointers.  Every tensor pointer is a DEVICE pointer (HIP device memory of
+ * the current device), including `scale`.  The caller owns every buffer; the
+ * library allocates nothing.  x, q and the bf16 outputs must be 16-byte
+ * aligned; alpha, scale and the workspace 4-byte aligned.
+ *
+ * Streams.  Every call only enqueues work on `stream` (NULL = the default
+ * stream) and returns; outputs are valid once the stream reaches that point.
+ * Calls that share a workspace must not run concurrently on different streams.
+ *
+ * Errors.  Arguments are checked before anything is enqueued; a failed check
+ * returns a nonzero status and enqueues nothing.  TACO_ERR_HIP reports a
+ * failed kernel launch (hipGetLastError).  A device fault surfaces at the
+ * caller's next synchronisation.  Inputs must be finite with |x| <= 2^56 and
+ * every nonzero block must hold an element of magnitude >= 2^-56; E must lie in
+ * [2^-40, 2^40].  Outside that domain results are unspecified (but no
+ * out-of-bounds access happens).
+ */
+#ifndef TACO_H
+#define TACO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t. */
+typedef struct ihipStream_t* taco_stream_t;
+
+typedef enum {
+  TACO_OK = 0,
+  TACO_ERR_NULL = 1,              /* a required pointer is NULL                    */
+  TACO_ERR_ALIGN = 2,             /* a pointer is not aligned as documented        */
+  TACO_ERR_SHAPE = 3,             /* tokens < 1, hidden < 1 or hidden % block != 0 */
+  TACO_ERR_UNSUPPORTED_BLOCK = 4, /* block not in {64, 128, 256}                   */
+  TACO_ERR_BAD_ENERGY = 5,        /* target energy not finite or out of range      */
+  TACO_ERR_WORKSPACE = 6,         /* workspace smaller than required               */
+  TACO_ERR_BAD_NPARTS = 7,        /* nparts outside [1, TACO_MAX_PARTS]            */
+  TACO_ERR_HIP = 8,               /* a HIP runtime call or kernel launch failed    */
+  TACO_ERR_BAD_ENGINE = 9         /* unknown value passed to taco_set_rotation_engine */
+} taco_status_t;
+
+/* How taco_compress evaluates the Hadamard rotation.  Both give the same
+ * values up to fp32 rounding order (and so the same codes except at rounding
+ * ties); they differ in which hardware unit does the work. */
+typedef enum {
+  TACO_ENGINE_AUTO = 0,           /* the faster one on this device (MFMA)          */
+  TACO_ENGINE_VALU = 1,           /* radix-2 butterflies on the vector ALUs + DPP  */
+  TACO_ENGINE_MFMA = 2            /* +-1 contraction on the bf16 matrix cores      */
+} taco_engine_t;
+
+#define TACO_MAX_PARTS 8
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* taco_status_string(taco_status_t status);
+
+/* Library version string, e.g. "0.2.0". */
+const char* taco_version(void);
+
+/* Select the rotation engine of taco_compress for the whole process (it is
+ * read when a call is made; calls already enqueued are unaffected).  Returns
+ * TACO_ERR_BAD_ENGINE for an unknown value.  Default: TACO_ENGINE_AUTO. */
+taco_status_t taco_set_rotation_engine(taco_engine_t engine);
+taco_engine_t taco_get_rotation_engine(void);
+
+/* Number of per-block ASH scales of a [tokens, hidden] tensor at this block
+ * size (tokens * hidden / block), or -1 if the shape or block is invalid. */
+int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block);
+
+/* Bytes of device workspace taco_compress needs for this shape (0 for an
+ * invalid shape).  The workspace holds per-workgroup partial maxima; it needs no
+ * initialisation and may be reused by later calls on the same stream. */
+size_t taco_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block);
+
+/*
+ * Compress: energy -> ASH scale -> Hadamard rotation -> DS scale -> FP8
+ * [TACO pt-summary, sections 2.B.1 (ASH), 2.B.2 (DS) and 2.B.3 (fused operator);
+ *  the per-tensor DS scale follows TACO zh-news, method section].
+ *   x_bf16          in : bf16 [tokens, hidden]
+ *   target_energy   in : E, the energy every block is rescaled to (1.0 typical)
+ *   q_fp8           out: uint8 [tokens, hidden]
+ *   alpha           out: fp32 [tokens, hidden / block]
+ *   scale           out: fp32 [1]
+ *   workspace       scratch of at least taco_compress_workspace_bytes() bytes
+ */
+taco_status_t taco_compress(const void* x_bf16, int64_t tokens, int64_t hidden,
+                            int32_t block, float target_energy, uint8_t* q_fp8,
+                            float* alpha, float* scale, void* workspace,
+                            size_t workspace_bytes, taco_stream_t stream);
+
+/*
+ * Decompress: decode -> undo s -> inverse rotation -> undo alpha -> bf16
+ * [TACO pt-summary, section 2.B.2: both scales reverse the process].
+ *   q_fp8, alpha, scale  in : the output of taco_compress (same shape / block)
+ *   y_bf16               out: bf16 [tokens, hidden], round to nearest even
+ */
+taco_status_t taco_decompress(const uint8_t* q_fp8, const float* alpha,
+                              const float* scale, int64_t tokens, int64_t hidden,
+                              int32_t block, void* y_bf16, taco_stream_t stream);
+
+/*
+ * Decompress-and-sum: the local reduction of the two-shot (reduce-scatter +
+ * all-gather) all-reduce [TACO pt-summary, section 2.B.3].
+ *   out = bf16( sum_p decompress(q_p, alpha_p, scale_p) ), summed in fp32 and
+ *   rounded once.
+ *   q_fp8, alpha, scale  HOST arrays of `nparts` DEVICE pointers (read during
+ *                        the call; the arrays may be freed when it returns)
+ *   nparts               1 .. TACO_MAX_PARTS
+ *   out_bf16             out: bf16 [tokens, hidden]; may not alias any input
+ */
+taco_status_t taco_decompress_sum(const uint8_t* const* q_fp8, const float* const* alpha,
+                                  const float* const* scale, int32_t nparts,
+                                  int64_t tokens, int64_t hidden, int32_t block,
+                                  void* out_bf16, taco_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TACO_H */

@@ -1,0 +1,87 @@
+"""The C-ABI library loads and exports every function include/taco.h declares.
+
+CPU only: these tests make no compute call.  The argument checks exercised
+here all fail before any HIP call, so fake (never dereferenced) pointer values
+are safe.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "taco.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(taco_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from fp8_compression_tensor_taco_amd import build
+    if not os.path.exists(build.LIB_PATH):
+        build.build_library(verbose=False)
+    from fp8_compression_tensor_taco_amd import load
+    return load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["taco_compress", "taco_decompress", "taco_decompress_sum", "taco_status_string",
+              "taco_num_scales", "taco_compress_workspace_bytes", "taco_version",
+              "taco_set_rotation_engine", "taco_get_rotation_engine"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_host_only_queries(lib):
+    assert lib.taco_version().decode().count(".") == 2
+    assert lib.taco_num_scales(4096, 4096, 128) == 4096 * 32
+    assert lib.taco_num_scales(4096, 1600, 64) == 4096 * 25
+    assert lib.taco_num_scales(4, 96, 64) == -1
+    assert lib.taco_num_scales(4, 128, 32) == -1
+    assert lib.taco_num_scales(0, 128, 64) == -1
+    assert lib.taco_compress_workspace_bytes(4096, 4096, 128) > 0
+    assert lib.taco_compress_workspace_bytes(4, 96, 64) == 0
+    for s in range(10):
+        assert lib.taco_status_string(s).decode().startswith("TACO_")
+    assert lib.taco_set_rotation_engine(7) == 9
+    for e in (1, 2, 0):
+        assert lib.taco_set_rotation_engine(e) == 0 and lib.taco_get_rotation_engine() == e
+
+
+FAKE = 0x10000        # 16-byte aligned, never dereferenced (every call below fails a check)
+
+
+def test_argument_checks_fail_before_any_launch(lib):
+    c = lib.taco_compress
+    ws = lib.taco_compress_workspace_bytes(8, 128, 64)
+    f = ctypes.c_float(1.0)
+    assert c(None, 8, 128, 64, f, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
+    assert c(FAKE + 2, 8, 128, 64, f, FAKE, FAKE, FAKE, FAKE, ws, None) == 2
+    assert c(FAKE, 8, 96, 64, f, FAKE, FAKE, FAKE, FAKE, ws, None) == 3
+    assert c(FAKE, 0, 128, 64, f, FAKE, FAKE, FAKE, FAKE, ws, None) == 3
+    assert c(FAKE, 8, 128, 32, f, FAKE, FAKE, FAKE, FAKE, ws, None) == 4
+    assert c(FAKE, 8, 128, 64, ctypes.c_float(0.0), FAKE, FAKE, FAKE, FAKE, ws, None) == 5
+    assert c(FAKE, 8, 128, 64, ctypes.c_float(float("nan")), FAKE, FAKE, FAKE, FAKE, ws, None) == 5
+    assert c(FAKE, 8, 128, 64, f, FAKE, FAKE, FAKE, FAKE, ws - 4, None) == 6
+    d = lib.taco_decompress
+    assert d(None, FAKE, FAKE, 8, 128, 64, FAKE, None) == 1
+    assert d(FAKE + 8, FAKE, FAKE, 8, 128, 64, FAKE, None) == 2
+    assert d(FAKE, FAKE, FAKE, 8, 128, 48, FAKE, None) == 4
+    s = lib.taco_decompress_sum
+    arr = (ctypes.c_void_p * 1)(FAKE)
+    assert s(arr, arr, arr, 0, 8, 128, 64, FAKE, None) == 7
+    assert s(arr, arr, arr, 9, 8, 128, 64, FAKE, None) == 7
+    assert s(arr, arr, arr, 1, 8, 100, 64, FAKE, None) == 3
+    nul = (ctypes.c_void_p * 1)(None)
+    assert s(nul, arr, arr, 1, 8, 128, 64, FAKE, None) == 1
+    assert s(arr, arr, arr, 1, 8, 128, 64, FAKE + 4, None) == 2

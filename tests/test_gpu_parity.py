@@ -1,0 +1,237 @@
+"""GPU parity: libtaco (through its C ABI, via the ctypes binding) against the oracle.
+
+Every case runs the GPU kernels and the fp64 oracle on the same seeded bf16
+input and compares element by element (see tests/parity.py for the bars):
+  * small sizes that span several workgroup tiles and end in a ragged tail;
+  * the full workload sizes, in the launch configuration bench.py times;
+  * edge cases: zero tensors and blocks, one-hot and constant blocks, a single
+    row, extreme magnitudes, negative zeros, every FP8 code.
+Inputs for decompress and decompress-sum are the oracle's own compressed
+triples, so no oracle input ever comes from the GPU path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_compression_tensor_taco_amd import workloads as W
+
+import parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def taco():
+    assert torch.cuda.is_available(), "GPU tests need a GPU (no CPU fallback exists)"
+    import fp8_compression_tensor_taco_amd as taco
+    taco.load()
+    return taco
+
+
+def to_gpu_bits(bits):
+    return W.from_bits(bits).cuda()
+
+
+def gpu_triple_np(q, a, s):
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), a.cpu().numpy(), np.float32(s.cpu().numpy()[0])
+
+
+# bf16 outputs: every element that differs from the oracle's must be justified by
+# the fp32 error bound at a bf16 rounding tie (tests/parity.py); where a block
+# mixes a heavy tail with near-zero values the fp32 rotation cancels and that
+# bound is wide, so the fraction of such elements is only capped loosely here.
+MAX_BF16_FRAC = 0.05
+
+
+ENGINES = ["mfma", "valu"]
+
+
+@pytest.fixture(params=ENGINES)
+def engine(request, taco):
+    taco.set_rotation_engine(request.param)
+    yield request.param
+    taco.set_rotation_engine("auto")
+
+
+def run_round_trip(taco, bits, block, E=1.0, max_code_frac=1e-4, max_bf16_frac=MAX_BF16_FRAC):
+    T, H = bits.shape
+    print(f"[case] compress/decompress shape=({T},{H}) block={block} E={E} "
+          f"engine={taco.get_rotation_engine()}", flush=True)
+    q_o, a_o, s_o = oracle.compress(bits, block, E)
+    x = to_gpu_bits(bits)
+    q_g, a_g, s_g = gpu_triple_np(*taco.compress(x, block, E))
+    parity.check_scales(a_g, s_g, a_o, s_o)
+    parity.check_codes(q_g, q_o, bits, a_o, s_o, block, max_frac=max_code_frac)
+    # decompress the oracle's triple on the GPU
+    trip = (torch.from_numpy(q_o).cuda(), torch.from_numpy(a_o).cuda(),
+            torch.tensor([s_o], dtype=torch.float32).cuda())
+    xh_g = W.bf16_bits(taco.decompress(*trip, block))
+    xh_o = oracle.decompress(q_o, a_o, s_o, block)
+    exact = oracle.decompress_f64(q_o, a_o, s_o, block)
+    parity.bf16_neighbours_ok(xh_g, xh_o, exact,
+                              parity.decompress_error_bound(q_o, a_o, s_o, block), max_bf16_frac)
+    # full GPU round trip against the oracle's round trip
+    rt = W.bf16_bits(taco.decompress(*[torch.from_numpy(np.atleast_1d(t)).cuda()
+                                       for t in (q_g, a_g, s_g)], block))
+    assert parity.rel_frobenius(rt, xh_o) <= 1e-3
+    return q_g, a_g, s_g
+
+
+# ------------------------------------------------------------------ small sizes
+SMALL = [("tiny", 256), ("tiny", 3), ("gpt2_1p5b", 37), ("gpt3_6p7b_act", 19),
+         ("gpt3_6p7b_grad", 21), ("qwen_7b", 23), ("dsum_part", 9)]
+
+
+@pytest.mark.parametrize("name,tokens", SMALL)
+def test_small_round_trip(taco, engine, name, tokens):
+    w = W.WORKLOADS[name]
+    bits = W.bf16_bits(W.make(name, seed=5, tokens=tokens))
+    run_round_trip(taco, bits, w.block)
+
+
+@pytest.mark.parametrize("block", [64, 128, 256])
+@pytest.mark.parametrize("tokens,hidden", [(1, 256), (5, 768), (131, 512)])
+def test_small_shapes_every_block(taco, engine, block, tokens, hidden):
+    rng = np.random.default_rng(tokens * hidden + block)
+    vals = rng.standard_normal((tokens, hidden)) * np.exp(rng.uniform(-6, 6, (tokens, 1)))
+    run_round_trip(taco, oracle.f64_to_bf16_bits(vals), block)
+
+
+@pytest.mark.parametrize("E", [1.0, 0.25, 37.5])
+def test_target_energy(taco, engine, E):
+    bits = W.bf16_bits(W.make("gpt3_6p7b_act", seed=2, tokens=16))
+    run_round_trip(taco, bits, 128, E)
+
+
+# ------------------------------------------------------------------ edge cases
+def test_zero_tensor(taco, engine):
+    bits = np.zeros((4, 256), dtype=np.uint16)
+    q, a, s = run_round_trip(taco, bits, 64)
+    assert s == 1.0 and np.all(a == 1.0) and np.all(parity.ordinal(q) == 0)
+
+
+def test_negative_zeros_and_zero_blocks(taco, engine):
+    rng = np.random.default_rng(0)
+    vals = rng.standard_normal((8, 512)) * 0.01
+    vals[2, :] = -0.0
+    vals[5, 128:256] = 0.0
+    run_round_trip(taco, oracle.f64_to_bf16_bits(vals), 128)
+
+
+@pytest.mark.parametrize("block", [64, 128, 256])
+def test_one_hot_and_constant_blocks(taco, engine, block):
+    vals = np.zeros((4, 2 * block))
+    vals.reshape(-1, block)[0, 3] = 0.75
+    vals.reshape(-1, block)[1, block - 1] = -3.0
+    vals.reshape(-1, block)[2, :] = 0.5
+    vals.reshape(-1, block)[3, :] = -2.0 ** -7
+    vals.reshape(-1, block)[4, 0] = 2.0 ** -5
+    vals.reshape(-1, block)[5, :] = np.linspace(-1, 1, block)
+    vals.reshape(-1, block)[6, ::7] = 1.0
+    run_round_trip(taco, oracle.f64_to_bf16_bits(vals), block)
+
+
+@pytest.mark.parametrize("scale_exp", [-50, -20, 20, 50])
+def test_extreme_magnitudes(taco, engine, scale_exp):
+    bits = W.bf16_bits(W.make("tiny", seed=9, tokens=8))
+    vals = oracle.bf16_bits_to_f64(bits) * 2.0 ** scale_exp
+    q, a, s = run_round_trip(taco, oracle.f64_to_bf16_bits(vals), 64)
+    # the GPU arithmetic is exactly invariant under power-of-two input scaling:
+    # same codes and s, alpha scaled by the inverse power
+    q0, a0, s0 = gpu_triple_np(*taco.compress(to_gpu_bits(bits), 64))
+    assert np.array_equal(q, q0) and s == s0
+    assert np.array_equal(a, a0 * np.float32(2.0 ** -scale_exp))
+
+
+def test_every_fp8_code_decodes_exactly(taco):
+    """Row r holds code r at position 0 and zeros elsewhere (alpha = s = 1), so
+    the decompressed row is decode(r) / sqrt(64) in every position."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    q = np.zeros((codes.size, 64), dtype=np.uint8)
+    q[:, 0] = codes
+    a = np.ones((codes.size, 1), dtype=np.float32)
+    out = taco.decompress(torch.from_numpy(q).cuda(), torch.from_numpy(a).cuda(),
+                          torch.ones(1, dtype=torch.float32).cuda(), 64)
+    got = oracle.bf16_bits_to_f64(W.bf16_bits(out))
+    want = oracle.e4m3_decode(codes) / 8.0
+    assert np.array_equal(got, np.repeat(want[:, None], 64, axis=1))
+
+
+def test_determinism(taco, engine):
+    x = W.make("gpt2_1p5b", seed=3, tokens=512).cuda()
+    r1 = [t.clone() for t in taco.compress(x, 64)]
+    for _ in range(20):
+        r2 = taco.compress(x, 64)
+        for a, b in zip(r1, r2):
+            assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ decompress-sum
+def run_decompress_sum(taco, part_bits, block):
+    T, H = part_bits[0].shape
+    print(f"[case] decompress_sum parts={len(part_bits)} shape=({T},{H}) block={block}", flush=True)
+    trip_o = [oracle.compress(b, block) for b in part_bits]
+    ref = oracle.decompress_sum(trip_o, block)
+    exact = sum(oracle.decompress_f64(*t, block) for t in trip_o)
+    gpu_parts = [(torch.from_numpy(q).cuda(), torch.from_numpy(a).cuda(),
+                  torch.tensor([s], dtype=torch.float32).cuda()) for q, a, s in trip_o]
+    got = W.bf16_bits(taco.decompress_sum(gpu_parts, block))
+    parity.bf16_neighbours_ok(got, ref, exact, parity.decompress_sum_error_bound(trip_o, block),
+                              MAX_BF16_FRAC)
+    assert parity.rel_frobenius(got, ref) <= 1e-3
+    # the GPU's own compressions summed on the GPU, against the oracle's sum
+    mine = [taco.compress(to_gpu_bits(b), block) for b in part_bits]
+    got2 = W.bf16_bits(taco.decompress_sum(mine, block))
+    assert parity.rel_frobenius(got2, ref) <= 1e-3
+
+
+@pytest.mark.parametrize("nparts", [1, 2, 3, 4, 8])
+def test_decompress_sum_small(taco, nparts):
+    parts = [W.bf16_bits(W.make("dsum_part", seed=p, tokens=7)) for p in range(nparts)]
+    run_decompress_sum(taco, parts, 256)
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_decompress_sum_other_blocks(taco, block):
+    parts = [W.bf16_bits(W.make("gpt3_6p7b_act", seed=p, tokens=11)) for p in range(4)]
+    run_decompress_sum(taco, parts, block)
+
+
+def test_decompress_sum_one_part_matches_decompress(taco):
+    """One part: the same reconstruction as decompress, up to the fp32 rounding
+    order (the sum applies 1/(alpha s) before the rotation, decompress after)."""
+    bits = W.bf16_bits(W.make("gpt3_6p7b_act", seed=1, tokens=64))
+    q, a, s = oracle.compress(bits, 128)
+    t = (torch.from_numpy(q).cuda(), torch.from_numpy(a).cuda(),
+         torch.tensor([s], dtype=torch.float32).cuda())
+    one = W.bf16_bits(taco.decompress_sum([t], 128))
+    ref = oracle.decompress(q, a, s, 128)
+    exact = oracle.decompress_f64(q, a, s, 128)
+    parity.bf16_neighbours_ok(one, ref, exact, parity.decompress_sum_error_bound([(q, a, s)], 128),
+                              MAX_BF16_FRAC)
+    assert parity.rel_frobenius(one, W.bf16_bits(taco.decompress(*t, 128))) <= 1e-3
+
+
+# ------------------------------------------------------------------ full sizes
+FULL = ["tiny", "gpt2_1p5b", "gpt3_6p7b_act", "gpt3_6p7b_grad", "qwen_7b"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_round_trip(taco, engine, name):
+    w = W.WORKLOADS[name]
+    seed = 1 if name == "gpt3_6p7b_grad" else 0
+    bits = W.bf16_bits(W.make(name, seed=seed))
+    run_round_trip(taco, bits, w.block)
+
+
+def test_full_size_decompress_sum_32_layers(taco):
+    """4 parts of [4096, 4096] at block 256; the same call repeated over 32
+    layer slots gives bitwise-identical outputs."""
+    parts = [W.bf16_bits(W.make("dsum_part", seed=p)) for p in range(4)]
+    run_decompress_sum(taco, parts, 256)
+    gp = [taco.compress(to_gpu_bits(b), 256) for b in parts]
+    outs = [taco.decompress_sum(gp, 256) for _ in range(32)]
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
