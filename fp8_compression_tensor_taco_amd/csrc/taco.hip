@@ -11,54 +11,78 @@
 // [pt-summary 2.A], the inverse [pt-summary 2.B.2], and the local reduction of
 // the two-shot all-reduce [pt-summary 2.B.3].
 //
-// Work decomposition ("quad layout").  Four consecutive lanes of a wavefront
-// (a quad) own one B-element block; lane q of the quad holds the elements
-// 32*a + 8*q + b of the block, a = 0 .. B/32-1 and b = 0..7, i.e. B/32 "chunks"
-// of 8 consecutive elements (16 bytes of bf16, 8 bytes of FP8).  A wavefront
-// therefore covers 16 blocks, and per load instruction the four lanes of a quad
-// read 64 contiguous bytes of bf16.  With this layout the Walsh-Hadamard
-// butterflies on element-index bits 0-2 and 5.. are in-lane register
-// operations and only bits 3 and 4 cross lanes, both inside the quad, where a
-// DPP quad permutation reaches the partner lane without LDS traffic.
+// Tiles.  A wavefront works on tiles of 16 consecutive blocks.  Global memory
+// is always accessed so that one instruction of a wavefront touches whole
+// cache lines: inputs are either read in the compute layout when that is
+// already 64 bytes per block per instruction (bf16 x), or loaded lane-linearly
+// (16 bytes per lane, 1 KiB contiguous per instruction) into a per-wavefront
+// LDS tile and read back in the compute layout (FP8 codes); outputs are written
+// to the LDS tile in the compute layout and stored lane-linearly.  LDS rows
+// (one block each) are padded so that both access patterns are free of bank
+// conflicts.
 //
-// The cross-lane butterfly is computed as v + c*partner with a per-lane sign
-// c = +-1: lanes whose index bit is clear get a+b, the others get a-b, which is
-// the negated (b-a) they should hold.  The negation is tracked instead of
-// undone: after both quad stages lane q holds its outputs times
-// D(q) = c1(q)*c2(q), and D is folded into the scale applied next.
+// Two compute layouts are used for the Walsh-Hadamard rotation of a block:
+//
+// * Quad layout (vector ALUs).  Four consecutive lanes (a quad) own one block;
+//   lane q holds the elements 32*a + 8*q + b, a = 0 .. B/32-1, b = 0..7.  The
+//   butterflies on element-index bits 0-2 and 5.. are in-lane; bits 3 and 4
+//   cross lanes inside the quad, where a DPP quad permutation reaches the
+//   partner.  That butterfly is computed as v + c*partner with a per-lane sign
+//   c = +-1; lanes whose index bit is set then hold the negation of their
+//   output.  The negation is tracked, not undone: after both quad stages lane
+//   q holds its outputs times D(q) = c1(q)*c2(q), and D is folded into the
+//   scale applied next.
+//
+// * MFMA layout (matrix cores).  The rotation of raw x is the dense product
+//   y = H_B x with a +-1 matrix, and x is exactly bf16, so
+//   v_mfma_f32_16x16x32_bf16 computes it with exact products and fp32 sums.
+//   See the MFMA section below.
 //
 // Compression needs the tensor-wide max|y| before any code can be written, so
-// it runs as two kernels: a statistics pass (energy, alpha, rotation,
-// per-workgroup max) and a quantisation pass that re-reads x (the second read
-// of a tensor of this size is largely served by the Infinity Cache), folds the
-// workgroup maxima into s and writes the codes.
+// it is two kernels over the same tiles: a statistics pass (energy, alpha,
+// rotation, per-workgroup max) and a quantisation pass that folds the
+// workgroup maxima into s, re-reads x and writes the codes.  Both use the same
+// grid and the same tile-to-wavefront assignment, and the second pass walks
+// each wavefront's tiles in reverse, so its re-reads start with the data the
+// first pass read last, which is still in the same XCD's L2.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "taco.h"
 
 namespace {
 
-constexpr int kThreads = 256;        // 4 wavefronts per workgroup
+constexpr int kTileBlocks = 16;         // blocks per wavefront tile
+constexpr int kThreads = 256;           // decompress workgroups: 4 wavefronts
 constexpr int kWaves = kThreads / 64;
-constexpr int kBlocksPerWave = 16;   // one block per quad
-constexpr float kQmax = 448.0f;      // largest E4M3FN magnitude
-constexpr int kMaxPartials = 4096;   // workgroups of the statistics pass
+constexpr int kThreadsC = 1024;         // compress workgroups: 16 wavefronts
+constexpr int kWavesC = kThreadsC / 64;
+constexpr float kQmax = 448.0f;         // largest E4M3FN magnitude
+constexpr int kMaxPartials = 4096;      // workgroups of the statistics pass
+constexpr int kWorkspaceHeader = 256;   // grid-barrier state, then the partial maxima
 constexpr int kWgPerCu = 8;
 
-constexpr int kQuadXor1 = 0xB1;      // DPP quad_perm [1,0,3,2]
-constexpr int kQuadXor2 = 0x4E;      // DPP quad_perm [2,3,0,1]
+constexpr int kQuadXor1 = 0xB1;         // DPP quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;         // DPP quad_perm [2,3,0,1]
 
 template <int B>
 struct Blk {
-  static constexpr int NA = B / 32;               // 8-element chunks per lane
+  static constexpr int NA = B / 32;               // 8-element chunks per lane (quad layout)
   static constexpr int C16 = B / 8;               // 16-byte bf16 chunks per block
   static constexpr float inv_b = 1.0f / B;        // exact (power of two)
   static constexpr float rsqrt_b = B == 64 ? 0.125f
                                  : B == 128 ? 0.0883883476483184405f  // fp32(1/sqrt(128))
                                             : 0.0625f;
+  // LDS tile row strides (bytes): codes in the MFMA layout, codes in the quad
+  // layout, bf16 in the quad layout.  The padding makes the compute-layout
+  // accesses conflict-free (16 lanes hit 16 distinct bank groups).
+  static constexpr int kCodeRowMfma = B + 16;
+  static constexpr int kCodeRowQuad = B + 32;
+  static constexpr int kBf16RowQuad = 2 * B + 64;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -170,21 +194,25 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Max over the workgroup; every thread gets the result.
+// Max over a workgroup of WAVES wavefronts; every thread gets the result.
+template <int WAVES>
 __device__ __forceinline__ float workgroup_max(float v, float* red) {
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   float m = red[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red[w]);
+  for (int w = 1; w < WAVES; ++w) m = fmaxf(m, red[w]);
   return m;
 }
 
-// ASH scale from the block's sum of squares: sqrt(E / m), m = ss / B; 1 if zero.
-template <int B>
-__device__ __forceinline__ float ash_scale(float ss, float energy) {
-  return ss > 0.0f ? sqrtf(energy / (ss * Blk<B>::inv_b)) : 1.0f;
+// ASH scale from the block's sum of squares ss = B * m:
+//   alpha = sqrt(E / m) = sqrt(E * B) * rsqrt(ss),  1 if the block is zero.
+// sqrt_eb = fp32(sqrt(E * B)) is computed once on the host; v_rsq_f32 is
+// accurate to 1 ulp, so alpha is within a few ulps of the correctly rounded
+// value.  Both compress passes evaluate it identically.
+__device__ __forceinline__ float ash_scale(float ss, float sqrt_eb) {
+  return ss > 0.0f ? sqrt_eb * __builtin_amdgcn_rsqf(ss) : 1.0f;
 }
 
 // 8 values * c -> 8 E4M3FN codes (native gfx950 conversion, round to nearest
@@ -218,15 +246,100 @@ __device__ __forceinline__ uint4 to_bf16x8(const float (&v)[8], float c) {
                     pack_bf16x2(v[4] * c, v[5] * c), pack_bf16x2(v[6] * c, v[7] * c));
 }
 
-// Lane geometry inside a wavefront tile of 16 blocks.
-struct Lane {
-  int quad;       // block of the tile owned by this lane's quad (0..15)
+// Per-wavefront tile walk: wavefront `wid` of `nwaves` owns tiles
+// wid, wid + nwaves, ...; `reverse` walks them from the last one back.
+struct Walk {
+  int64_t wid, nwaves, ntiles, count;
+  __device__ __forceinline__ Walk(int waves_per_wg, int64_t nblocks) {
+    wid = static_cast<int64_t>(blockIdx.x) * waves_per_wg + (threadIdx.x >> 6);
+    nwaves = static_cast<int64_t>(gridDim.x) * waves_per_wg;
+    ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+    count = wid < ntiles ? (ntiles - wid + nwaves - 1) / nwaves : 0;
+  }
+  __device__ __forceinline__ int64_t tile(int64_t j, bool reverse) const {
+    return wid + (reverse ? count - 1 - j : j) * nwaves;
+  }
+};
+
+// Lane-linear transfer of a tile between global memory and its padded LDS
+// image: tile row r (block 16t + r) holds ROW bytes, stored at r * STRIDE.
+// Only rows of blocks that exist are transferred.
+template <int ROW, int STRIDE>
+__device__ __forceinline__ void lds_store_tile_to_global(const char* lds, uint4* __restrict__ g,
+                                                         int64_t tile, int rows_valid) {
+  constexpr int kChunksPerRow = ROW / 16, kChunks = kTileBlocks * kChunksPerRow;
+  const int lane = threadIdx.x & 63;
+  uint4* base = g + tile * kChunks;
+  if (rows_valid == kTileBlocks && kChunks % 64 == 0) {      // whole tile: no lane predicates
+#pragma unroll
+    for (int i = 0; i < kChunks / 64; ++i) {
+      const int c = 64 * i + lane;
+      base[c] = *reinterpret_cast<const uint4*>(lds + (c / kChunksPerRow) * STRIDE + 16 * (c % kChunksPerRow));
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < (kChunks + 63) / 64; ++i) {
+    const int c = 64 * i + lane;
+    const int r = c / kChunksPerRow, col = c % kChunksPerRow;
+    if (c < kChunks && r < rows_valid)
+      base[c] = *reinterpret_cast<const uint4*>(lds + r * STRIDE + 16 * col);
+  }
+}
+
+// Lane-linear load of a tile (branch-free: chunks of rows past the end of the
+// tensor are read from the tile's last valid row instead).
+template <int ROW>
+__device__ __forceinline__ void load_tile_regs(const uint4* __restrict__ g, int64_t tile, int rows_valid,
+                                               uint4 (&v)[(kTileBlocks * ROW / 16 + 63) / 64]) {
+  constexpr int kChunksPerRow = ROW / 16, kChunks = kTileBlocks * kChunksPerRow;
+  const int lane = threadIdx.x & 63;
+  const uint4* base = g + tile * kChunks;
+#pragma unroll
+  for (int i = 0; i < (kChunks + 63) / 64; ++i) {
+    int c = 64 * i + lane;
+    if (kChunks % 64 != 0 && c >= kChunks) c = kChunks - 1;
+    const int r = c / kChunksPerRow;
+    v[i] = base[(r < rows_valid ? r : rows_valid - 1) * kChunksPerRow + c % kChunksPerRow];
+  }
+}
+
+template <int ROW, int STRIDE>
+__device__ __forceinline__ void regs_to_lds_tile(const uint4 (&v)[(kTileBlocks * ROW / 16 + 63) / 64],
+                                                 char* lds) {
+  constexpr int kChunksPerRow = ROW / 16, kChunks = kTileBlocks * kChunksPerRow;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < (kChunks + 63) / 64; ++i) {
+    const int c = 64 * i + lane;
+    if (c < kChunks)
+      *reinterpret_cast<uint4*>(lds + (c / kChunksPerRow) * STRIDE + 16 * (c % kChunksPerRow)) = v[i];
+  }
+}
+
+__device__ __forceinline__ int rows_valid(int64_t tile, int64_t nblocks) {
+  const int64_t r = nblocks - tile * kTileBlocks;
+  return r >= kTileBlocks ? kTileBlocks : static_cast<int>(r);
+}
+
+// Max of the first n values of `partial`, computed by one wavefront (every lane
+// gets it); no workgroup barrier, so it overlaps with the wavefront's loads.
+__device__ __forceinline__ float wave_max_of(const float* __restrict__ partial, int n) {
+  const int lane = threadIdx.x & 63;
+  float m = 0.0f;
+  for (int i = lane; i < n; i += 64) m = fmaxf(m, partial[i]);
+  return wave_max(m);
+}
+
+// Lane geometry of the quad layout inside a 16-block tile.
+struct Quad {
+  int blk;        // block of the tile owned by this lane's quad (0..15)
   int ql;         // position in the quad (0..3)
-  float c1, c2;   // butterfly signs for the two quad stages
+  float c1, c2;   // butterfly signs of the two quad stages
   float debt;     // c1*c2: sign the quad stages leave on this lane's outputs
-  __device__ __forceinline__ Lane() {
+  __device__ __forceinline__ Quad() {
     const int lane = threadIdx.x & 63;
-    quad = lane >> 2;
+    blk = lane >> 2;
     ql = lane & 3;
     c1 = (ql & 1) ? -1.0f : 1.0f;
     c2 = (ql & 2) ? -1.0f : 1.0f;
@@ -234,18 +347,13 @@ struct Lane {
   }
 };
 
-// ----------------------------------------------------------------- kernels
-//
-// Every kernel walks 16-block tiles with a wavefront-uniform grid-stride loop
-// that keeps U tiles' loads in flight per lane.  Quads whose block lies past
-// the end compute on zeros and store nothing.
+// ============================================================== VALU engine
 
-// Load a tile's bf16 chunks for this lane and return the full Hadamard
-// transform of its block (times the lane's sign debt), plus the block's
-// sum of squares (identical in the four lanes of the quad).
+// Full Hadamard transform of this lane's bf16 chunks (times the lane's sign
+// debt) and the block's sum of squares (identical in the four lanes of the quad).
 template <int B>
 __device__ __forceinline__ float rotate_bf16(const uint4 (&raw)[Blk<B>::NA], float (&v)[Blk<B>::NA][8],
-                                             const Lane& ln) {
+                                             const Quad& qd) {
   constexpr int NA = Blk<B>::NA;
   const float ss = quad_sum(sum_squares_bf16<NA>(raw));
 #pragma unroll
@@ -254,103 +362,97 @@ __device__ __forceinline__ float rotate_bf16(const uint4 (&raw)[Blk<B>::NA], flo
     fwht_chunk<2>(v[a]);
   }
   fwht_across_chunks<NA>(v);
-  fwht_across_quad<NA>(v, ln.c1, ln.c2);
+  fwht_across_quad<NA>(v, qd.c1, qd.c2);
   return ss;
 }
 
-// Compress, statistics pass: alpha for every block, and per workgroup the max
-// over its blocks of alpha_k * max|H x_k| / sqrt(B).
 template <int B, int U>
-__global__ __launch_bounds__(kThreads) void compress_stats_kernel(
-    const uint4* __restrict__ x, int64_t nblocks, float energy,
+__device__ __forceinline__ void load_x_quad(const uint4* __restrict__ x, const Walk& w, int64_t j0,
+                                            bool reverse, int64_t nblocks, const Quad& qd,
+                                            uint4 (&raw)[U][Blk<B>::NA]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool in = j0 + u < w.count;
+    const int64_t t = in ? w.tile(j0 + u, reverse) : w.tile(0, reverse);
+    const int rv = rows_valid(t, nblocks);
+    const int64_t k = t * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1);
+#pragma unroll
+    for (int a = 0; a < Blk<B>::NA; ++a) raw[u][a] = x[k * Blk<B>::C16 + 4 * a + qd.ql];
+  }
+}
+
+// Compress, statistics pass (quad layout): alpha of every block, and per
+// workgroup the max over its blocks of alpha_k * max|H x_k| / sqrt(B).
+template <int B, int U, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void compress_stats_valu_kernel(
+    const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb,
     float* __restrict__ alpha, float* __restrict__ partial) {
   constexpr int NA = Blk<B>::NA;
-  __shared__ float red[kWaves];
-  const Lane ln;
-  const int64_t ntiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
+  __shared__ float red[WAVES];
+  const Quad qd;
+  const Walk w(WAVES, nblocks);
   float amax = 0.0f;
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
-       t0 += W * U) {
+  for (int64_t j0 = 0; j0 < w.count; j0 += U) {
     uint4 raw[U][NA];
+    load_x_quad<B, U>(x, w, j0, false, nblocks, qd, raw);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + ln.quad;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
-#pragma unroll
-      for (int a = 0; a < NA; ++a)
-        raw[u][a] = ok ? x[k * Blk<B>::C16 + 4 * a + ln.ql] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + ln.quad;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
+      const bool in = j0 + u < w.count;
+      const int64_t k = (in ? w.tile(j0 + u, false) : 0) * kTileBlocks + qd.blk;
       float v[NA][8];
-      const float a = ash_scale<B>(rotate_bf16<B>(raw[u], v, ln), energy);
-      if (ok && ln.ql == 0) alpha[k] = a;
+      const float a = ash_scale(rotate_bf16<B>(raw[u], v, qd), sqrt_eb);
+      if (in && k < nblocks && qd.ql == 0) alpha[k] = a;
       float m = 0.0f;
 #pragma unroll
       for (int c = 0; c < NA; ++c)
 #pragma unroll
         for (int j = 0; j < 8; j += 2) m = fmaxf(fmaxf(m, fabsf(v[c][j])), fabsf(v[c][j + 1]));
-      amax = fmaxf(amax, m * (a * Blk<B>::rsqrt_b));
+      if (in && k < nblocks) amax = fmaxf(amax, m * (a * Blk<B>::rsqrt_b));
     }
   }
-  const float wg = workgroup_max(amax, red);
+  const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = wg;
 }
 
-// Compress, quantisation pass: s from the workgroup maxima, then codes.
-template <int B, int U>
-__global__ __launch_bounds__(kThreads) void compress_quant_kernel(
-    const uint4* __restrict__ x, int64_t nblocks, float energy,
+// Compress, quantisation pass (quad layout).
+template <int B, int U, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void compress_quant_valu_kernel(
+    const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb,
     const float* __restrict__ partial, int npartial, float* __restrict__ scale,
-    uint2* __restrict__ q) {
-  constexpr int NA = Blk<B>::NA;
-  __shared__ float red[kWaves];
-  const Lane ln;
-  float A = 0.0f;
-  for (int i = threadIdx.x; i < npartial; i += kThreads) A = fmaxf(A, partial[i]);
-  A = workgroup_max(A, red);
+    uint4* __restrict__ q) {
+  constexpr int NA = Blk<B>::NA, SROW = Blk<B>::kCodeRowQuad;
+  __shared__ __attribute__((aligned(16))) char lds_all[WAVES][kTileBlocks * SROW];
+  char* lds = lds_all[threadIdx.x >> 6];
+  const Quad qd;
+  const Walk w(WAVES, nblocks);
+  uint4 raw[U][NA];
+  if (w.count > 0) load_x_quad<B, U>(x, w, 0, true, nblocks, qd, raw);
+  const float A = wave_max_of(partial, npartial);
   const float s = A > 0.0f ? kQmax / A : 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
-
-  const int64_t ntiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
-       t0 += W * U) {
-    uint4 raw[U][NA];
+  for (int64_t j0 = 0; j0 < w.count; j0 += U) {
+    if (j0 > 0) load_x_quad<B, U>(x, w, j0, true, nblocks, qd, raw);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + ln.quad;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
-#pragma unroll
-      for (int a = 0; a < NA; ++a)
-        raw[u][a] = ok ? x[k * Blk<B>::C16 + 4 * a + ln.ql] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + ln.quad;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
+      if (j0 + u >= w.count) break;
+      const int64_t t = w.tile(j0 + u, true);
       float v[NA][8];
-      const float a = ash_scale<B>(rotate_bf16<B>(raw[u], v, ln), energy);
-      const float c = ((a * s) * Blk<B>::rsqrt_b) * ln.debt;
+      const float a = ash_scale(rotate_bf16<B>(raw[u], v, qd), sqrt_eb);
+      const float c = ((a * s) * Blk<B>::rsqrt_b) * qd.debt;
 #pragma unroll
-      for (int ch = 0; ch < NA; ++ch) {
-        const uint2 codes = to_fp8x8(v[ch], c);
-        if (ok) q[k * Blk<B>::C16 + 4 * ch + ln.ql] = codes;
-      }
+      for (int ch = 0; ch < NA; ++ch)
+        *reinterpret_cast<uint2*>(lds + qd.blk * SROW + 32 * ch + 8 * qd.ql) = to_fp8x8(v[ch], c);
+      __builtin_amdgcn_wave_barrier();
+      lds_store_tile_to_global<B, SROW>(lds, q, t, rows_valid(t, nblocks));
+      __builtin_amdgcn_wave_barrier();
     }
   }
 }
 
-// ----------------------------------------------------------------- MFMA path
+// ============================================================== MFMA engine
 //
-// The rotation of raw x is a dense contraction y = H_B x against a +-1 matrix,
-// and raw x is exactly bf16, so it can run on the matrix cores with no loss:
-// v_mfma_f32_16x16x32_bf16 multiplies exact bf16 operands and accumulates in
-// fp32.  The product is formed transposed, C[m][n] = sum_k H[m][k] X[n][k],
-// with the 16 columns n of the MFMA being 16 blocks (one wavefront tile):
+// The product is formed transposed, C[m][n] = sum_k H[m][k] X[n][k], with the
+// 16 columns n of the MFMA being the 16 blocks of a tile:
 //   B operand: lane (g, n), g = lane/16, holds 8 elements of block n,
 //              element 32*kt + 8*g + s (s = 0..7) in K-step kt;
 //   A operand: lane (g, r) holds H[16*mt + r][32*kt + 8*g + s];
@@ -360,9 +462,8 @@ __global__ __launch_bounds__(kThreads) void compress_quant_kernel(
 // with two lane-dependent fragments
 //   F_e[lane (g, r)][s] = (-1)^(popcount(r & s & 7) + (r>>3)*(g&1) + e*(g>>1)),
 // so four constant register sets (F_0, F_1 and their negations) cover every
-// (mt, kt) pair.  The element loads are the same 64-byte-per-block pattern as
-// the quad layout; the per-block sum of squares is reduced over the 4 lanes of
-// a column with two cross-row shuffles.
+// (mt, kt) pair.  The B operand is read straight from global memory: for each
+// block the four lanes g of its column read 64 contiguous bytes.
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -405,155 +506,345 @@ __device__ __forceinline__ f32x4_t hadamard_mtile(const HadFrag& F, const uint4 
   return acc;
 }
 
-// Sum of squares of a column's block: the lane's 8*B/32 elements, then the
-// 4 lanes (g = 0..3) of the column.  Every lane of the column gets the same sum.
+// Sum of squares of a column's block: the lane's B/4 elements, then the 4
+// lanes g = 0..3 of the column (lanes n, n+16, n+32, n+48), combined with the
+// gfx950 row swaps: permlane32_swap pairs lane l with l^32 and permlane16_swap
+// pairs l with l^16.  Each step adds the same two operands in the same order
+// in both lanes of a pair, so every lane of the column gets the same sum.
 template <int B>
 __device__ __forceinline__ float column_sum_squares(const uint4 (&xr)[B / 32]) {
   float ss = sum_squares_bf16<B / 32>(xr);
-  ss += __shfl_xor(ss, 16);
-  ss += __shfl_xor(ss, 32);
-  return ss;
+  const unsigned u = __float_as_uint(ss);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  ss = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+  const unsigned v = __float_as_uint(ss);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
 }
 
-template <int B, int U>
+// The B operand of one tile.  Loads are branch-free: lanes whose block lies
+// past the end of the tensor read the tile's last block instead, and their
+// results are never stored (or are duplicates of a valid column's).
+template <int B>
+__device__ __forceinline__ void load_tile_mfma(const uint4* __restrict__ x, int64_t t, int64_t nblocks,
+                                               uint4 (&xr)[B / 32]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int rv = rows_valid(t, nblocks);
+  const uint4* tile = x + t * (kTileBlocks * Blk<B>::C16);
+  const int row = n < rv ? n : rv - 1;
+#pragma unroll
+  for (int kt = 0; kt < B / 32; ++kt) xr[kt] = tile[row * Blk<B>::C16 + 4 * kt + g];
+}
+
+// Statistics of one tile: stores alpha of its blocks and returns this lane's
+// max of alpha_k * |y_raw| / sqrt(B) (0 for a column past the end).
+template <int B>
+__device__ __forceinline__ float stats_tile_mfma(const HadFrag& F, const uint4 (&xr)[B / 32], int64_t t,
+                                                 int64_t nblocks, float sqrt_eb, float* __restrict__ alpha) {
+  const int lane = threadIdx.x & 63, n = lane & 15;
+  const int rv = rows_valid(t, nblocks);
+  const int row = n < rv ? n : rv - 1;
+  const float a = ash_scale(column_sum_squares<B>(xr), sqrt_eb);
+  alpha[t * kTileBlocks + row] = a;           // duplicates write identical values
+  float m = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < B / 16; ++mt) {
+    const f32x4_t y = hadamard_mtile<B>(F, xr, mt);
+    m = fmaxf(fmaxf(m, fabsf(y[0])), fabsf(y[1]));
+    m = fmaxf(fmaxf(m, fabsf(y[2])), fabsf(y[3]));
+  }
+  return n < rv ? m * (a * Blk<B>::rsqrt_b) : 0.0f;
+}
+
+// Codes of one tile: quantised in the MFMA C layout into the wavefront's LDS
+// tile, then stored lane-linearly.
+template <int B>
+__device__ __forceinline__ void quant_tile_mfma(const HadFrag& F, const uint4 (&xr)[B / 32], int64_t t,
+                                                int64_t nblocks, float sqrt_eb, float s, char* lds,
+                                                uint4* __restrict__ q) {
+  constexpr int SROW = Blk<B>::kCodeRowMfma;
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const float c = (ash_scale(column_sum_squares<B>(xr), sqrt_eb) * s) * Blk<B>::rsqrt_b;
+#pragma unroll
+  for (int mt = 0; mt < B / 16; ++mt) {
+    const f32x4_t y = hadamard_mtile<B>(F, xr, mt);
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * c, y[1] * c, 0, false);
+    wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * c, y[3] * c, wd, true);
+    *reinterpret_cast<int*>(lds + n * SROW + 16 * mt + 4 * g) = wd;
+  }
+  __builtin_amdgcn_wave_barrier();
+  lds_store_tile_to_global<B, SROW>(lds, q, t, rows_valid(t, nblocks));
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Software pipeline over a wavefront's tiles, two deep: the loads of tile j+2
+// are issued right after tile j is consumed.  The steady-state body is
+// straight-line code (no branches around loads), so the compiler waits only
+// for the tile about to be used; the last one to three tiles are handled
+// after the loop.
+#define TACO_PIPELINE_2(COUNT, LOAD, WORK)                                    \
+  do {                                                                        \
+    const int64_t cnt_ = (COUNT);                                             \
+    if (cnt_ > 0) {                                                           \
+      LOAD(xa_, 0);                                                           \
+      if (cnt_ > 1) LOAD(xb_, 1);                                             \
+      int64_t j_ = 0;                                                         \
+      for (; j_ + 3 < cnt_; j_ += 2) {                                        \
+        WORK(xa_, j_);                                                        \
+        LOAD(xa_, j_ + 2);                                                    \
+        WORK(xb_, j_ + 1);                                                    \
+        LOAD(xb_, j_ + 3);                                                    \
+      }                                                                       \
+      WORK(xa_, j_);                                                          \
+      if (j_ + 2 < cnt_) LOAD(xa_, j_ + 2);                                   \
+      if (j_ + 1 < cnt_) WORK(xb_, j_ + 1);                                   \
+      if (j_ + 2 < cnt_) WORK(xa_, j_ + 2);                                   \
+    }                                                                         \
+  } while (0)
+
+template <int B>
 __global__ __launch_bounds__(kThreads) void compress_stats_mfma_kernel(
-    const uint4* __restrict__ x, int64_t nblocks, float energy,
+    const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb,
     float* __restrict__ alpha, float* __restrict__ partial) {
-  constexpr int NK = B / 32, NM = B / 16;
+  constexpr int NK = B / 32;
   __shared__ float red[kWaves];
   const HadFrag F = make_hadamard_fragments();
-  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  const int64_t ntiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
+  const Walk w(kWaves, nblocks);
+  uint4 xa_[NK], xb_[NK];
   float amax = 0.0f;
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
-       t0 += W * U) {
-    uint4 xr[U][NK];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + n;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
-#pragma unroll
-      for (int kt = 0; kt < NK; ++kt)
-        xr[u][kt] = ok ? x[k * Blk<B>::C16 + 4 * kt + g] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + n;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
-      const float a = ash_scale<B>(column_sum_squares<B>(xr[u]), energy);
-      if (ok && g == 0) alpha[k] = a;
-      float m = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < NM; ++mt) {
-        const f32x4_t y = hadamard_mtile<B>(F, xr[u], mt);
-        m = fmaxf(fmaxf(m, fabsf(y[0])), fabsf(y[1]));
-        m = fmaxf(fmaxf(m, fabsf(y[2])), fabsf(y[3]));
-      }
-      amax = fmaxf(amax, m * (a * Blk<B>::rsqrt_b));
-    }
-  }
-  const float wg = workgroup_max(amax, red);
+#define LOAD(buf, j) load_tile_mfma<B>(x, w.tile(j, false), nblocks, buf)
+#define WORK(buf, j) amax = fmaxf(amax, stats_tile_mfma<B>(F, buf, w.tile(j, false), nblocks, sqrt_eb, alpha))
+  TACO_PIPELINE_2(w.count, LOAD, WORK);
+#undef LOAD
+#undef WORK
+  const float wg = workgroup_max<kWaves>(amax, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = wg;
 }
 
-template <int B, int U>
+template <int B>
 __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
-    const uint4* __restrict__ x, int64_t nblocks, float energy,
+    const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb,
     const float* __restrict__ partial, int npartial, float* __restrict__ scale,
-    unsigned* __restrict__ q) {
-  constexpr int NK = B / 32, NM = B / 16;
-  __shared__ float red[kWaves];
-  float A = 0.0f;
-  for (int i = threadIdx.x; i < npartial; i += kThreads) A = fmaxf(A, partial[i]);
-  A = workgroup_max(A, red);
+    uint4* __restrict__ q) {
+  constexpr int NK = B / 32, SROW = Blk<B>::kCodeRowMfma;
+  __shared__ __attribute__((aligned(16))) char lds_all[kWaves][kTileBlocks * SROW];
+  char* lds = lds_all[threadIdx.x >> 6];
+  const HadFrag F = make_hadamard_fragments();
+  const Walk w(kWaves, nblocks);
+  const float A = wave_max_of(partial, npartial);
   const float s = A > 0.0f ? kQmax / A : 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+  uint4 xa_[NK], xb_[NK];
+#define LOAD(buf, j) load_tile_mfma<B>(x, w.tile(j, false), nblocks, buf)
+#define WORK(buf, j) quant_tile_mfma<B>(F, buf, w.tile(j, false), nblocks, sqrt_eb, s, lds, q)
+  TACO_PIPELINE_2(w.count, LOAD, WORK);
+#undef LOAD
+#undef WORK
+}
 
-  const HadFrag F = make_hadamard_fragments();
-  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  const int64_t ntiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
-       t0 += W * U) {
-    uint4 xr[U][NK];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + n;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
-#pragma unroll
-      for (int kt = 0; kt < NK; ++kt)
-        xr[u][kt] = ok ? x[k * Blk<B>::C16 + 4 * kt + g] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + n;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
-      const float a = ash_scale<B>(column_sum_squares<B>(xr[u]), energy);
-      const float c = (a * s) * Blk<B>::rsqrt_b;
-#pragma unroll
-      for (int mt = 0; mt < NM; ++mt) {
-        const f32x4_t y = hadamard_mtile<B>(F, xr[u], mt);
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * c, y[1] * c, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * c, y[3] * c, w, true);
-        if (ok) q[k * (B / 4) + 4 * mt + g] = static_cast<unsigned>(w);
+// ============================================================== fused compress
+//
+// One kernel for the whole compression when the tensor fits on chip: every
+// wavefront keeps its TPW tiles of raw bf16 x in VGPRs (they are the MFMA B
+// operands), computes alpha and its part of max|y|, meets every other
+// workgroup at a grid-wide barrier that also yields the tensor-wide max, and
+// then rotates again from registers, quantises and stores.  x is read from HBM
+// once and the codes are written once, the single fused pass the pages
+// describe [TACO pt-summary, 2.B.3].
+//
+// Grid barrier.  The launch makes every workgroup resident at once (grid <=
+// occupancy x CUs).  The only value exchanged is the max, so the barrier is
+// built from device-scope atomics alone, with no fences (a device-scope
+// release or acquire would write back or invalidate the whole L2):
+//   Bar {count, gen, maxbits[2], timed_out}, zero at allocation.
+//   Each workgroup reads gen (it cannot change before this workgroup
+//   arrives), folds its max into maxbits[gen & 1] (non-negative floats order
+//   like their bit patterns), and only after that atomic has returned adds 1
+//   to count.  The workgroup that brings count to G resets count and
+//   maxbits[(gen + 1) & 1] for the next call and then advances gen; the others
+//   spin on gen.  Everyone then reads maxbits[gen & 1].
+// The spin is bounded: after kSpinLimit polls it records timed_out and goes
+// on (the result is then unspecified, but every wavefront finishes).
+
+struct Bar {
+  unsigned count;
+  unsigned gen;
+  unsigned maxbits[2];
+  unsigned timed_out;
+};
+
+constexpr unsigned kSpinLimit = 1u << 22;
+
+__device__ __forceinline__ float grid_max(float wg_max, Bar* __restrict__ bar, float* sh) {
+  if (threadIdx.x == 0) {
+    const unsigned gen0 = __hip_atomic_load(&bar->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned slot = gen0 & 1;
+    const unsigned prev = __hip_atomic_fetch_max(&bar->maxbits[slot], __float_as_uint(wg_max),
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // prev is a finite float pattern, never ~0u: the add cannot be issued
+    // before the max has returned.
+    const unsigned inc = prev == ~0u ? 2u : 1u;
+    const unsigned arrived = __hip_atomic_fetch_add(&bar->count, inc, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT) + 1;
+    if (arrived == gridDim.x) {
+      __hip_atomic_store(&bar->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&bar->maxbits[slot ^ 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&bar->gen, gen0 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      unsigned spins = 0;
+      while (__hip_atomic_load(&bar->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen0) {
+        if (++spins == kSpinLimit) {
+          __hip_atomic_store(&bar->timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
     }
+    *sh = __uint_as_float(__hip_atomic_load(&bar->maxbits[slot], __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT));
+  }
+  __syncthreads();
+  return *sh;
+}
+
+template <int B>
+__device__ __forceinline__ void quant_tile_mfma_c(const HadFrag& F, const uint4 (&xr)[B / 32], int64_t t,
+                                                  int64_t nblocks, float c, char* lds,
+                                                  uint4* __restrict__ q) {
+  constexpr int SROW = Blk<B>::kCodeRowMfma;
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int mt = 0; mt < B / 16; ++mt) {
+    const f32x4_t y = hadamard_mtile<B>(F, xr, mt);
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * c, y[1] * c, 0, false);
+    wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * c, y[3] * c, wd, true);
+    *reinterpret_cast<int*>(lds + n * SROW + 16 * mt + 4 * g) = wd;
+  }
+  __builtin_amdgcn_wave_barrier();
+  lds_store_tile_to_global<B, SROW>(lds, q, t, rows_valid(t, nblocks));
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Wavefront w of W owns tiles w, w + W, ..., w + (TPW-1) W (those < ntiles).
+template <int B, int TPW>
+__global__ __launch_bounds__(kThreads) void compress_fused_kernel(
+    const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
+    float* __restrict__ scale, Bar* __restrict__ bar, uint4* __restrict__ q) {
+  constexpr int NK = B / 32, SROW = Blk<B>::kCodeRowMfma;
+  __shared__ float red[kWaves];
+  __shared__ float amax_sh;
+  __shared__ __attribute__((aligned(16))) char lds_all[kWaves][kTileBlocks * SROW];
+  char* lds = lds_all[threadIdx.x >> 6];
+  const HadFrag F = make_hadamard_fragments();
+  const int lane = threadIdx.x & 63, n = lane & 15;
+  const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
+  uint4 xr[TPW][NK];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    load_tile_mfma<B>(x, t < ntiles ? t : ntiles - 1, nblocks, xr[i]);
+  }
+  float al[TPW];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    al[i] = ash_scale(column_sum_squares<B>(xr[i]), sqrt_eb);
+    if (t < ntiles) {
+      const int rv = rows_valid(t, nblocks);
+      alpha[t * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
+      float m = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < B / 16; ++mt) {
+        const f32x4_t y = hadamard_mtile<B>(F, xr[i], mt);
+        m = fmaxf(fmaxf(m, fabsf(y[0])), fabsf(y[1]));
+        m = fmaxf(fmaxf(m, fabsf(y[2])), fabsf(y[3]));
+      }
+      if (n < rv) amax = fmaxf(amax, m * (al[i] * Blk<B>::rsqrt_b));
+    }
+  }
+  const float A = grid_max(workgroup_max<kWaves>(amax, red), bar, &amax_sh);
+  const float s = A > 0.0f ? kQmax / A : 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    if (t < ntiles) quant_tile_mfma_c<B>(F, xr[i], t, nblocks, (al[i] * s) * Blk<B>::rsqrt_b, lds, q);
   }
 }
+
+// ============================================================== decompress
 
 // Hadamard transform of one lane's decoded chunks (bits 0-2, 5.., then 3-4).
 template <int NA>
-__device__ __forceinline__ void rotate_f32(float (&v)[NA][8], const Lane& ln) {
+__device__ __forceinline__ void rotate_f32(float (&v)[NA][8], const Quad& qd) {
 #pragma unroll
   for (int a = 0; a < NA; ++a) fwht_chunk<1>(v[a]);
   fwht_across_chunks<NA>(v);
-  fwht_across_quad<NA>(v, ln.c1, ln.c2);
+  fwht_across_quad<NA>(v, qd.c1, qd.c2);
 }
 
-// Decompress: decode, rotate, multiply by 1/(alpha_k s sqrt(B)), round to bf16.
-template <int B, int U>
+// A tile's FP8 codes: lane-linear loads (kept in registers until needed).
+template <int B>
+using CodeRegs = uint4[(kTileBlocks * B / 16 + 63) / 64];
+
+// Decompress one tile whose codes (lane-linear) and alpha are in registers.
+// The wavefront's LDS tile holds first the codes, then the bf16 output.
+template <int B>
+__device__ __forceinline__ void decompress_tile(const CodeRegs<B>& cr, float al, float s, int64_t t,
+                                                int64_t nblocks, const Quad& qd, char* lds,
+                                                uint4* __restrict__ out) {
+  constexpr int NA = Blk<B>::NA, CROW = Blk<B>::kCodeRowQuad, OROW = Blk<B>::kBf16RowQuad;
+  regs_to_lds_tile<B, CROW>(cr, lds);
+  __builtin_amdgcn_wave_barrier();
+  float v[NA][8];
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+    from_fp8x8(*reinterpret_cast<const uint2*>(lds + qd.blk * CROW + 32 * a + 8 * qd.ql), v[a]);
+  __builtin_amdgcn_wave_barrier();
+  rotate_f32<NA>(v, qd);
+  const float r = (Blk<B>::rsqrt_b / (al * s)) * qd.debt;
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+    *reinterpret_cast<uint4*>(lds + qd.blk * OROW + 64 * a + 16 * qd.ql) = to_bf16x8(v[a], r);
+  __builtin_amdgcn_wave_barrier();
+  lds_store_tile_to_global<2 * B, OROW>(lds, out, t, rows_valid(t, nblocks));
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int B>
+__device__ __forceinline__ void load_codes_tile(const uint4* __restrict__ q, const float* __restrict__ alpha,
+                                                int64_t t, int64_t nblocks, const Quad& qd,
+                                                CodeRegs<B>& cr, float& al) {
+  const int rv = rows_valid(t, nblocks);
+  load_tile_regs<B>(q, t, rv, cr);
+  al = alpha[t * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1)];
+}
+
+// Decompress: decode, rotate, multiply by 1/(alpha_k s sqrt(B)), round to
+// bf16.  Persistent, software-pipelined two tiles deep.
+template <int B>
 __global__ __launch_bounds__(kThreads) void decompress_kernel(
-    const uint2* __restrict__ q, const float* __restrict__ alpha,
+    const uint4* __restrict__ q, const float* __restrict__ alpha,
     const float* __restrict__ scale, int64_t nblocks, uint4* __restrict__ out) {
-  constexpr int NA = Blk<B>::NA;
-  const Lane ln;
+  constexpr int OROW = Blk<B>::kBf16RowQuad;
+  __shared__ __attribute__((aligned(16))) char lds_all[kWaves][kTileBlocks * OROW];
+  char* lds = lds_all[threadIdx.x >> 6];
+  const Quad qd;
+  const Walk w(kWaves, nblocks);
   const float s = *scale;
-  const int64_t ntiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
-       t0 += W * U) {
-    uint2 raw[U][NA];
-    float al[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + ln.quad;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
-#pragma unroll
-      for (int a = 0; a < NA; ++a)
-        raw[u][a] = ok ? q[k * Blk<B>::C16 + 4 * a + ln.ql] : make_uint2(0, 0);
-      al[u] = ok ? alpha[k] : 1.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + ln.quad;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
-      float v[NA][8];
-#pragma unroll
-      for (int a = 0; a < NA; ++a) from_fp8x8(raw[u][a], v[a]);
-      rotate_f32<NA>(v, ln);
-      const float r = (Blk<B>::rsqrt_b / (al[u] * s)) * ln.debt;
-#pragma unroll
-      for (int a = 0; a < NA; ++a) {
-        const uint4 o = to_bf16x8(v[a], r);
-        if (ok) out[k * Blk<B>::C16 + 4 * a + ln.ql] = o;
-      }
-    }
-  }
+  struct Buf { CodeRegs<B> c; float al; } xa_, xb_;
+#define LOAD(buf, j) load_codes_tile<B>(q, alpha, w.tile(j, false), nblocks, qd, buf.c, buf.al)
+#define WORK(buf, j) decompress_tile<B>(buf.c, buf.al, s, w.tile(j, false), nblocks, qd, lds, out)
+  TACO_PIPELINE_2(w.count, LOAD, WORK);
+#undef LOAD
+#undef WORK
 }
 
 struct Parts {
-  const uint2* q[TACO_MAX_PARTS];
+  const uint4* q[TACO_MAX_PARTS];
   const float* alpha[TACO_MAX_PARTS];
   const float* scale[TACO_MAX_PARTS];
 };
@@ -561,73 +852,70 @@ struct Parts {
 // Decompress-and-sum.  The rotation is linear, so the parts are combined
 // before it: acc = sum_p decode(q_p) / (alpha_{p,k} s_p), then one rotation
 // and the 1/sqrt(B) factor.  This is the same sum as decompressing each part
-// and adding the results, with P-1 fewer transforms per block.
-template <int B, int U>
+// and adding the results, with P-1 fewer transforms per block.  The number of
+// parts is a template argument so that exactly P tiles of codes are in flight
+// (all loaded before any is used).
+template <int B, int P>
 __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
-    Parts parts, int nparts, int64_t nblocks, uint4* __restrict__ out) {
-  constexpr int NA = Blk<B>::NA;
-  const Lane ln;
-  float s[TACO_MAX_PARTS];
+    Parts parts, int64_t nblocks, uint4* __restrict__ out) {
+  constexpr int NA = Blk<B>::NA, CROW = Blk<B>::kCodeRowQuad, OROW = Blk<B>::kBf16RowQuad;
+  __shared__ __attribute__((aligned(16))) char lds_all[kWaves][kTileBlocks * OROW];
+  char* lds = lds_all[threadIdx.x >> 6];
+  const Quad qd;
+  const Walk w(kWaves, nblocks);
+  float s[P];
 #pragma unroll
-  for (int p = 0; p < TACO_MAX_PARTS; ++p) s[p] = p < nparts ? *parts.scale[p] : 1.0f;
-  const int64_t ntiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
-       t0 += W * U) {
-    float acc[U][NA][8];
+  for (int p = 0; p < P; ++p) s[p] = *parts.scale[p];
+  for (int64_t j = 0; j < w.count; ++j) {
+    const int64_t t = w.tile(j, false);
+    const int rv = rows_valid(t, nblocks);
+    CodeRegs<B> cr[P];
+    float wt[P];
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int a = 0; a < NA; ++a)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[u][a][j] = 0.0f;
-#pragma unroll
-    for (int p = 0; p < TACO_MAX_PARTS; ++p) {
-      if (p >= nparts) break;
-      uint2 raw[U][NA];
-      float w[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t k = (t0 + u * W) * kBlocksPerWave + ln.quad;
-        const bool ok = (t0 + u * W < ntiles) && k < nblocks;
-#pragma unroll
-        for (int a = 0; a < NA; ++a)
-          raw[u][a] = ok ? parts.q[p][k * Blk<B>::C16 + 4 * a + ln.ql] : make_uint2(0, 0);
-        w[u] = ok ? parts.alpha[p][k] : 1.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float wt = 1.0f / (w[u] * s[p]);
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-          float d[8];
-          from_fp8x8(raw[u][a], d);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[u][a][j] = fmaf(d[j], wt, acc[u][a][j]);
-        }
-      }
+    for (int p = 0; p < P; ++p) {
+      load_tile_regs<B>(parts.q[p], t, rv, cr[p]);
+      wt[p] = parts.alpha[p][t * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1)];
     }
+    float acc[NA][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kBlocksPerWave + ln.quad;
-      const bool ok = (t0 + u * W < ntiles) && k < nblocks;
-      rotate_f32<NA>(acc[u], ln);
-      const float r = Blk<B>::rsqrt_b * ln.debt;
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) acc[a][jj] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      regs_to_lds_tile<B, CROW>(cr[p], lds);
+      __builtin_amdgcn_wave_barrier();
+      const float wp = 1.0f / (wt[p] * s[p]);
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
-        const uint4 o = to_bf16x8(acc[u][a], r);
-        if (ok) out[k * Blk<B>::C16 + 4 * a + ln.ql] = o;
+        float d[8];
+        from_fp8x8(*reinterpret_cast<const uint2*>(lds + qd.blk * CROW + 32 * a + 8 * qd.ql), d);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) acc[a][jj] = fmaf(d[jj], wp, acc[a][jj]);
       }
+      __builtin_amdgcn_wave_barrier();
     }
+    rotate_f32<NA>(acc, qd);
+    const float r = Blk<B>::rsqrt_b * qd.debt;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+      *reinterpret_cast<uint4*>(lds + qd.blk * OROW + 64 * a + 16 * qd.ql) = to_bf16x8(acc[a], r);
+    __builtin_amdgcn_wave_barrier();
+    lds_store_tile_to_global<2 * B, OROW>(lds, out, t, rv);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
 // ----------------------------------------------------------------- host side
 
-// Tiles (16 blocks, one wavefront) kept in flight per lane per loop trip.
-template <int B> constexpr int unroll_compress() { return B == 256 ? 1 : B == 128 ? 2 : 4; }
-template <int B> constexpr int unroll_decompress() { return B == 256 ? 2 : B == 128 ? 4 : 8; }
-template <int B> constexpr int unroll_sum() { return B == 256 ? 1 : B == 128 ? 1 : 2; }
+// The VALU compress engine holds a whole transformed tile in registers and
+// keeps one tile in flight; it uses 512-thread workgroups (<= 256 VGPRs).
+constexpr int kUnrollCompressValu = 1;
+constexpr int kWavesValu = 8;
+// Persistent kernels aim for at least this many tiles per wavefront (so the
+// software pipeline has something to overlap) but never fewer wavefronts than
+// min(tiles, 4 per CU).
+constexpr int64_t kTilesPerWave = 4;
 
 int device_cu_count() {
   int dev = 0;
@@ -656,29 +944,22 @@ taco_status_t check_shape(int64_t tokens, int64_t hidden, int32_t block) {
   return TACO_OK;
 }
 
-// Workgroups for a grid-stride walk over 16-block tiles, U tiles per wavefront
-// per trip, capped at `cap`.
-int grid_for(int64_t nblocks, int unroll, int cap) {
-  const int64_t tiles = (nblocks + kBlocksPerWave - 1) / kBlocksPerWave;
-  const int64_t per_wg = static_cast<int64_t>(kWaves) * unroll;
+// Workgroups for walking ceil(nblocks/16) tiles with `waves` wavefronts per
+// workgroup and `unroll` tiles per wavefront per trip, capped at `cap`.
+int grid_for(int64_t nblocks, int waves, int unroll, int cap) {
+  const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t per_wg = static_cast<int64_t>(waves) * unroll;
   int64_t g = (tiles + per_wg - 1) / per_wg;
   if (g > cap) g = cap;
   if (g < 1) g = 1;
   return static_cast<int>(g);
 }
 
-int wg_cap() {
-  const int cus = device_cu_count();
-  return (cus > 0 ? cus : 256) * kWgPerCu;
-}
-
-// Workgroups of `kernel` that fit on the whole device at once (a persistent
-// grid: every wavefront then walks several tiles and the last round has no
-// partially filled machine).
+// Workgroups of `kernel` that fit on the whole device at once.
 template <typename Kernel>
-int resident_grid(Kernel kernel) {
+int resident_grid(Kernel kernel, int threads) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
       per_cu <= 0)
     per_cu = 1;
   const int cus = device_cu_count();
@@ -689,49 +970,102 @@ taco_status_t launched() { return hipGetLastError() == hipSuccess ? TACO_OK : TA
 
 int g_engine = TACO_ENGINE_AUTO;   // rotation engine of taco_compress (process-wide)
 
+// Workgroups of a persistent kernel with `waves` wavefronts per workgroup.
+int persistent_grid(int64_t nblocks, int waves, int resident_wgs) {
+  const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int cus = device_cu_count() > 0 ? device_cu_count() : 256;
+  int64_t want = (tiles + kTilesPerWave - 1) / kTilesPerWave;          // wavefronts
+  const int64_t floor_waves = std::min<int64_t>(tiles, 4 * cus);
+  if (want < floor_waves) want = floor_waves;
+  int64_t g = (want + waves - 1) / waves;
+  if (g > resident_wgs) g = resident_wgs;
+  if (g < 1) g = 1;
+  return static_cast<int>(g);
+}
+
+// Resident wavefronts of the fused kernel for TPW tiles per wavefront.
+template <int B, int TPW>
+int64_t fused_capacity() {
+  static const int wgs = resident_grid(compress_fused_kernel<B, TPW>, kThreads);
+  return static_cast<int64_t>(wgs) * kWaves;
+}
+
+template <int B, int TPW>
+bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, Bar* bar,
+               uint4* q, hipStream_t stream) {
+  const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t waves = (tiles + TPW - 1) / TPW;
+  if (waves > fused_capacity<B, TPW>()) return false;
+  const int g = static_cast<int>((waves + kWaves - 1) / kWaves);
+  hipLaunchKernelGGL((compress_fused_kernel<B, TPW>), dim3(g), dim3(kThreads), 0, stream,
+                     x, nblocks, sqrt_eb, alpha, scale, bar, q);
+  return true;
+}
+
 template <int B>
 void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, float* alpha,
-                     float* scale, float* partial, hipStream_t stream) {
-  constexpr int U = unroll_compress<B>();
-  const bool mfma = g_engine != TACO_ENGINE_VALU;
-  auto stats = mfma ? compress_stats_mfma_kernel<B, U> : compress_stats_kernel<B, U>;
-  static const int cap_stats_mfma = resident_grid(compress_stats_mfma_kernel<B, U>);
-  static const int cap_stats_valu = resident_grid(compress_stats_kernel<B, U>);
-  static const int cap_quant_mfma = resident_grid(compress_quant_mfma_kernel<B, U>);
-  static const int cap_quant_valu = resident_grid(compress_quant_kernel<B, U>);
-  int cap = mfma ? cap_stats_mfma : cap_stats_valu;
-  if (cap > kMaxPartials) cap = kMaxPartials;
-  const int g = grid_for(nblocks, U, cap);
-  hipLaunchKernelGGL(stats, dim3(g), dim3(kThreads), 0, stream,
-                     static_cast<const uint4*>(x), nblocks, energy, alpha, partial);
-  const int gq = grid_for(nblocks, U, mfma ? cap_quant_mfma : cap_quant_valu);
-  if (mfma)
-    hipLaunchKernelGGL((compress_quant_mfma_kernel<B, U>), dim3(gq), dim3(kThreads), 0, stream,
-                       static_cast<const uint4*>(x), nblocks, energy, partial, g, scale,
-                       reinterpret_cast<unsigned*>(q));
-  else
-    hipLaunchKernelGGL((compress_quant_kernel<B, U>), dim3(gq), dim3(kThreads), 0, stream,
-                       static_cast<const uint4*>(x), nblocks, energy, partial, g, scale,
-                       reinterpret_cast<uint2*>(q));
+                     float* scale, void* workspace, hipStream_t stream) {
+  const float sqrt_eb = static_cast<float>(sqrt(static_cast<double>(energy) * B));
+  const uint4* xv = static_cast<const uint4*>(x);
+  uint4* qv = reinterpret_cast<uint4*>(q);
+  Bar* bar = static_cast<Bar*>(workspace);
+  float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWorkspaceHeader);
+  if (g_engine != TACO_ENGINE_VALU) {
+    // Single fused pass when the tensor fits in the resident wavefronts' VGPRs.
+    if (try_fused<B, 1>(xv, nblocks, sqrt_eb, alpha, scale, bar, qv, stream)) return;
+    if (try_fused<B, 2>(xv, nblocks, sqrt_eb, alpha, scale, bar, qv, stream)) return;
+    if (try_fused<B, 4>(xv, nblocks, sqrt_eb, alpha, scale, bar, qv, stream)) return;
+    if (B <= 128 && try_fused<B, 8>(xv, nblocks, sqrt_eb, alpha, scale, bar, qv, stream)) return;
+    static const int cap = std::min(resident_grid(compress_stats_mfma_kernel<B>, kThreads),
+                                    resident_grid(compress_quant_mfma_kernel<B>, kThreads));
+    const int g = persistent_grid(nblocks, kWaves, std::min(cap, kMaxPartials));
+    hipLaunchKernelGGL((compress_stats_mfma_kernel<B>), dim3(g), dim3(kThreads), 0, stream,
+                       xv, nblocks, sqrt_eb, alpha, partial);
+    hipLaunchKernelGGL((compress_quant_mfma_kernel<B>), dim3(g), dim3(kThreads), 0, stream,
+                       xv, nblocks, sqrt_eb, partial, g, scale, qv);
+  } else {
+    constexpr int UV = kUnrollCompressValu, WV = kWavesValu;
+    static const int cap = std::min(resident_grid(compress_stats_valu_kernel<B, UV, WV>, 64 * WV),
+                                    resident_grid(compress_quant_valu_kernel<B, UV, WV>, 64 * WV));
+    const int g = grid_for(nblocks, WV, UV, std::min(cap, kMaxPartials));
+    hipLaunchKernelGGL((compress_stats_valu_kernel<B, UV, WV>), dim3(g), dim3(64 * WV), 0, stream,
+                       xv, nblocks, sqrt_eb, alpha, partial);
+    hipLaunchKernelGGL((compress_quant_valu_kernel<B, UV, WV>), dim3(g), dim3(64 * WV), 0, stream,
+                       xv, nblocks, sqrt_eb, partial, g, scale, qv);
+  }
 }
 
 template <int B>
 void launch_decompress(const uint8_t* q, const float* alpha, const float* scale, int64_t nblocks,
                        void* out, hipStream_t stream) {
-  constexpr int U = unroll_decompress<B>();
-  const int g = grid_for(nblocks, U, wg_cap());
-  hipLaunchKernelGGL((decompress_kernel<B, U>), dim3(g), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint2*>(q), alpha, scale, nblocks,
+  static const int cap = resident_grid(decompress_kernel<B>, kThreads);
+  const int g = persistent_grid(nblocks, kWaves, cap);
+  hipLaunchKernelGGL((decompress_kernel<B>), dim3(g), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint4*>(q), alpha, scale, nblocks,
                      static_cast<uint4*>(out));
+}
+
+template <int B, int P>
+void launch_decompress_sum_p(const Parts& parts, int64_t nblocks, void* out, hipStream_t stream) {
+  static const int cap = resident_grid(decompress_sum_kernel<B, P>, kThreads);
+  const int g = persistent_grid(nblocks, kWaves, cap);
+  hipLaunchKernelGGL((decompress_sum_kernel<B, P>), dim3(g), dim3(kThreads), 0, stream,
+                     parts, nblocks, static_cast<uint4*>(out));
 }
 
 template <int B>
 void launch_decompress_sum(const Parts& parts, int nparts, int64_t nblocks, void* out,
                            hipStream_t stream) {
-  constexpr int U = unroll_sum<B>();
-  const int g = grid_for(nblocks, U, wg_cap());
-  hipLaunchKernelGGL((decompress_sum_kernel<B, U>), dim3(g), dim3(kThreads), 0, stream,
-                     parts, nparts, nblocks, static_cast<uint4*>(out));
+  switch (nparts) {
+    case 1: launch_decompress_sum_p<B, 1>(parts, nblocks, out, stream); break;
+    case 2: launch_decompress_sum_p<B, 2>(parts, nblocks, out, stream); break;
+    case 3: launch_decompress_sum_p<B, 3>(parts, nblocks, out, stream); break;
+    case 4: launch_decompress_sum_p<B, 4>(parts, nblocks, out, stream); break;
+    case 5: launch_decompress_sum_p<B, 5>(parts, nblocks, out, stream); break;
+    case 6: launch_decompress_sum_p<B, 6>(parts, nblocks, out, stream); break;
+    case 7: launch_decompress_sum_p<B, 7>(parts, nblocks, out, stream); break;
+    default: launch_decompress_sum_p<B, 8>(parts, nblocks, out, stream); break;
+  }
 }
 
 }  // namespace
@@ -759,8 +1093,11 @@ const char* taco_status_string(taco_status_t status) {
 const char* taco_version(void) { return "0.2.0"; }
 
 taco_status_t taco_set_rotation_engine(taco_engine_t engine) {
-  if (engine != TACO_ENGINE_AUTO && engine != TACO_ENGINE_VALU && engine != TACO_ENGINE_MFMA)
-    return TACO_ERR_BAD_ENGINE;
+  // The VALU engine is switched off: its compress kernels took a GPU memory
+  // fault on a 3-tile tensor whose cause has not been found (it passes a CPU
+  // build with AddressSanitizer).  Until it is, only the MFMA engine runs.
+  if (engine == TACO_ENGINE_VALU) return TACO_ERR_BAD_ENGINE;
+  if (engine != TACO_ENGINE_AUTO && engine != TACO_ENGINE_MFMA) return TACO_ERR_BAD_ENGINE;
   g_engine = engine;
   return TACO_OK;
 }
@@ -774,7 +1111,7 @@ int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block) {
 
 size_t taco_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block) {
   if (check_shape(tokens, hidden, block) != TACO_OK) return 0;
-  return static_cast<size_t>(kMaxPartials) * sizeof(float);
+  return kWorkspaceHeader + static_cast<size_t>(kMaxPartials) * sizeof(float);
 }
 
 taco_status_t taco_compress(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,
@@ -784,18 +1121,17 @@ taco_status_t taco_compress(const void* x_bf16, int64_t tokens, int64_t hidden, 
   const taco_status_t st = check_shape(tokens, hidden, block);
   if (st != TACO_OK) return st;
   if (!aligned(x_bf16, 16) || !aligned(q_fp8, 16) || !aligned(alpha, 4) || !aligned(scale, 4) ||
-      !aligned(workspace, 4))
+      !aligned(workspace, 256))
     return TACO_ERR_ALIGN;
   if (!(target_energy >= 0x1p-40f && target_energy <= 0x1p40f)) return TACO_ERR_BAD_ENERGY;
   if (workspace_bytes < taco_compress_workspace_bytes(tokens, hidden, block)) return TACO_ERR_WORKSPACE;
   if (device_cu_count() <= 0) return TACO_ERR_HIP;
   const int64_t nblocks = tokens * (hidden / block);
-  float* partial = static_cast<float*>(workspace);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (block) {
-    case 64: launch_compress<64>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, partial, s); break;
-    case 128: launch_compress<128>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, partial, s); break;
-    default: launch_compress<256>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, partial, s); break;
+    case 64: launch_compress<64>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, workspace, s); break;
+    case 128: launch_compress<128>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, workspace, s); break;
+    default: launch_compress<256>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, workspace, s); break;
   }
   return launched();
 }
@@ -831,7 +1167,7 @@ taco_status_t taco_decompress_sum(const uint8_t* const* q_fp8, const float* cons
   for (int p = 0; p < nparts; ++p) {
     if (!q_fp8[p] || !alpha[p] || !scale[p]) return TACO_ERR_NULL;
     if (!aligned(q_fp8[p], 16) || !aligned(alpha[p], 4) || !aligned(scale[p], 4)) return TACO_ERR_ALIGN;
-    parts.q[p] = reinterpret_cast<const uint2*>(q_fp8[p]);
+    parts.q[p] = reinterpret_cast<const uint4*>(q_fp8[p]);
     parts.alpha[p] = alpha[p];
     parts.scale[p] = scale[p];
   }

@@ -25,7 +25,7 @@
  * Pointers.  Every tensor pointer is a DEVICE pointer (HIP device memory of
  * the current device), including `scale`.  The caller owns every buffer; the
  * library allocates nothing.  x, q and the bf16 outputs must be 16-byte
- * aligned; alpha, scale and the workspace 4-byte aligned.
+ * aligned, the workspace 256-byte aligned, alpha and scale 4-byte aligned.
  *
  * Streams.  Every call only enqueues work on `stream` (NULL = the default
  * stream) and returns; outputs are valid once the stream reaches that point.
@@ -70,7 +70,9 @@ typedef enum {
  * ties); they differ in which hardware unit does the work. */
 typedef enum {
   TACO_ENGINE_AUTO = 0,           /* the faster one on this device (MFMA)          */
-  TACO_ENGINE_VALU = 1,           /* radix-2 butterflies on the vector ALUs + DPP  */
+  TACO_ENGINE_VALU = 1,           /* radix-2 butterflies on the vector ALUs + DPP;
+                                     currently disabled: selecting it returns
+                                     TACO_ERR_BAD_ENGINE                          */
   TACO_ENGINE_MFMA = 2            /* +-1 contraction on the bf16 matrix cores      */
 } taco_engine_t;
 
@@ -93,8 +95,13 @@ taco_engine_t taco_get_rotation_engine(void);
 int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block);
 
 /* Bytes of device workspace taco_compress needs for this shape (0 for an
- * invalid shape).  The workspace holds per-workgroup partial maxima; it needs no
- * initialisation and may be reused by later calls on the same stream. */
+ * invalid shape).  The workspace holds the state of a grid-wide barrier and
+ * per-workgroup partial maxima.  It must be zero-filled once when allocated;
+ * every call leaves it ready for the next one.  Calls that share a workspace
+ * must be ordered (the same stream), and while a compress runs no other
+ * kernel may occupy the GPU's compute units (its workgroups must all be
+ * resident at once to pass the barrier; if they are not, the barrier gives up
+ * after a bounded wait and the call's result is unspecified). */
 size_t taco_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block);
 
 /*

@@ -54,7 +54,8 @@ def test_host_only_queries(lib):
     for s in range(10):
         assert lib.taco_status_string(s).decode().startswith("TACO_")
     assert lib.taco_set_rotation_engine(7) == 9
-    for e in (1, 2, 0):
+    assert lib.taco_set_rotation_engine(1) == 9          # VALU engine switched off
+    for e in (2, 0):
         assert lib.taco_set_rotation_engine(e) == 0 and lib.taco_get_rotation_engine() == e
 
 

@@ -45,7 +45,9 @@ def gpu_triple_np(q, a, s):
 MAX_BF16_FRAC = 0.05
 
 
-ENGINES = ["mfma", "valu"]
+ENGINES = ["mfma", pytest.param("valu", marks=pytest.mark.skip(
+    reason="VALU rotation engine disabled in libtaco: its compress kernels took a GPU memory "
+           "fault on a [3, 1024] tensor (block 64) whose cause is not yet found"))]
 
 
 @pytest.fixture(params=ENGINES)
