@@ -9,7 +9,9 @@ from ._binding import (  # noqa: F401
     TacoError,
     compress,
     get_rotation_engine,
+    get_single_pass,
     set_rotation_engine,
+    set_single_pass,
     decompress,
     decompress_sum,
     library_path,
@@ -20,6 +22,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "TACO_MAX_PARTS", "TacoError", "compress", "get_rotation_engine", "set_rotation_engine", "decompress", "decompress_sum",
-    "library_path", "load", "num_scales", "version", "workspace_bytes",
+    "TACO_MAX_PARTS", "TacoError", "compress", "decompress", "decompress_sum", "get_rotation_engine",
+    "get_single_pass", "library_path", "load", "num_scales", "set_rotation_engine", "set_single_pass",
+    "version", "workspace_bytes",
 ]

@@ -65,6 +65,10 @@ def load() -> ctypes.CDLL:
         lib.taco_set_rotation_engine.argtypes = [ctypes.c_int]
         lib.taco_get_rotation_engine.restype = ctypes.c_int
         lib.taco_get_rotation_engine.argtypes = []
+        lib.taco_set_single_pass.restype = None
+        lib.taco_set_single_pass.argtypes = [ctypes.c_int]
+        lib.taco_get_single_pass.restype = ctypes.c_int
+        lib.taco_get_single_pass.argtypes = []
         lib.taco_num_scales.restype = _i64
         lib.taco_num_scales.argtypes = [_i64, _i64, _i32]
         lib.taco_compress_workspace_bytes.restype = ctypes.c_size_t
@@ -134,6 +138,16 @@ def set_rotation_engine(name: str) -> None:
 def get_rotation_engine() -> str:
     v = load().taco_get_rotation_engine()
     return {i: n for n, i in ENGINES.items()}[v]
+
+
+def set_single_pass(enable: bool) -> None:
+    """Fused single-pass compress when the tensor fits on chip (default True);
+    False forces the two-kernel path.  Both give identical results."""
+    load().taco_set_single_pass(1 if enable else 0)
+
+
+def get_single_pass() -> bool:
+    return bool(load().taco_get_single_pass())
 
 
 def num_scales(tokens: int, hidden: int, block: int) -> int:

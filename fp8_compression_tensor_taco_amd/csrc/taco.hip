@@ -11,40 +11,37 @@
 // [pt-summary 2.A], the inverse [pt-summary 2.B.2], and the local reduction of
 // the two-shot all-reduce [pt-summary 2.B.3].
 //
-// Tiles.  A wavefront works on tiles of 16 consecutive blocks.  Global memory
-// is always accessed so that one instruction of a wavefront touches whole
-// cache lines: inputs are either read in the compute layout when that is
-// already 64 bytes per block per instruction (bf16 x), or loaded lane-linearly
-// (16 bytes per lane, 1 KiB contiguous per instruction) into a per-wavefront
-// LDS tile and read back in the compute layout (FP8 codes); outputs are written
-// to the LDS tile in the compute layout and stored lane-linearly.  LDS rows
-// (one block each) are padded so that both access patterns are free of bank
-// conflicts.
+// Tiles.  A wavefront works on tiles of 16 consecutive blocks.  Every global
+// access instruction of a wavefront covers whole 64-byte segments: bf16 x is
+// read in the MFMA layout (64 contiguous bytes per block per instruction),
+// FP8 codes and bf16 outputs of decompression move in the quad layout (32
+// and 64 contiguous bytes per quad), and compression codes, which the MFMA
+// layout would scatter in 4-byte pieces, are staged through a padded
+// per-wavefront LDS tile and stored lane-linearly (1 KiB per instruction).
 //
 // Two compute layouts are used for the Walsh-Hadamard rotation of a block:
 //
-// * Quad layout (vector ALUs).  Four consecutive lanes (a quad) own one block;
-//   lane q holds the elements 32*a + 8*q + b, a = 0 .. B/32-1, b = 0..7.  The
-//   butterflies on element-index bits 0-2 and 5.. are in-lane; bits 3 and 4
-//   cross lanes inside the quad, where a DPP quad permutation reaches the
-//   partner.  That butterfly is computed as v + c*partner with a per-lane sign
-//   c = +-1; lanes whose index bit is set then hold the negation of their
-//   output.  The negation is tracked, not undone: after both quad stages lane
-//   q holds its outputs times D(q) = c1(q)*c2(q), and D is folded into the
-//   scale applied next.
+// * Quad layout (vector ALUs, decompression).  Four consecutive lanes (a
+//   quad) own one block; lane q holds the elements 32*a + 8*q + b,
+//   a = 0 .. B/32-1, b = 0..7.  The butterflies on element-index bits 0-2 and
+//   5.. are in-lane; bits 3 and 4 cross lanes inside the quad, where a DPP
+//   quad permutation reaches the partner.  That butterfly is computed as
+//   v + c*partner with a per-lane sign c = +-1; lanes whose index bit is set
+//   then hold the negation of their output.  The negation is tracked, not
+//   undone: after both quad stages lane q holds its outputs times
+//   D(q) = c1(q)*c2(q), and D is folded into the scale applied next.
 //
-// * MFMA layout (matrix cores).  The rotation of raw x is the dense product
-//   y = H_B x with a +-1 matrix, and x is exactly bf16, so
+// * MFMA layout (matrix cores, compression).  The rotation of raw x is the
+//   dense product y = H_B x with a +-1 matrix, and x is exactly bf16, so
 //   v_mfma_f32_16x16x32_bf16 computes it with exact products and fp32 sums.
 //   See the MFMA section below.
 //
-// Compression needs the tensor-wide max|y| before any code can be written, so
-// it is two kernels over the same tiles: a statistics pass (energy, alpha,
-// rotation, per-workgroup max) and a quantisation pass that folds the
-// workgroup maxima into s, re-reads x and writes the codes.  Both use the same
-// grid and the same tile-to-wavefront assignment, and the second pass walks
-// each wavefront's tiles in reverse, so its re-reads start with the data the
-// first pass read last, which is still in the same XCD's L2.
+// Compression needs the tensor-wide max|y| before any code can be written.
+// When the tensor's rotated blocks fit in the registers of the resident
+// wavefronts it is one kernel with a grid-wide barrier (see the fused
+// section); otherwise two kernels over the same tiles: a statistics pass
+// (energy, alpha, rotation, per-workgroup max) and a quantisation pass that
+// folds the workgroup maxima into s, re-reads x and writes the codes.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -63,8 +60,6 @@ constexpr int kThreadsC = 1024;         // compress workgroups: 16 wavefronts
 constexpr int kWavesC = kThreadsC / 64;
 constexpr float kQmax = 448.0f;         // largest E4M3FN magnitude
 constexpr int kMaxPartials = 4096;      // workgroups of the statistics pass
-constexpr int kWorkspaceHeader = 256;   // grid-barrier state, then the partial maxima
-constexpr int kWgPerCu = 8;
 
 constexpr int kQuadXor1 = 0xB1;         // DPP quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;         // DPP quad_perm [2,3,0,1]
@@ -77,12 +72,9 @@ struct Blk {
   static constexpr float rsqrt_b = B == 64 ? 0.125f
                                  : B == 128 ? 0.0883883476483184405f  // fp32(1/sqrt(128))
                                             : 0.0625f;
-  // LDS tile row strides (bytes): codes in the MFMA layout, codes in the quad
-  // layout, bf16 in the quad layout.  The padding makes the compute-layout
-  // accesses conflict-free (16 lanes hit 16 distinct bank groups).
+  // LDS tile row stride (bytes) of codes in the MFMA layout; the padding makes
+  // the compute-layout writes conflict-free (16 lanes hit 16 bank groups).
   static constexpr int kCodeRowMfma = B + 16;
-  static constexpr int kCodeRowQuad = B + 32;
-  static constexpr int kBf16RowQuad = 2 * B + 64;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -120,16 +112,6 @@ __device__ __forceinline__ float sum_squares_bf16(const uint4 (&u)[NC]) {
 #pragma unroll
   for (int c = 1; c < kChains; ++c) ss += acc[c];
   return ss;
-}
-
-// bf16 -> fp32 fused with the first butterfly (index bit 0): for each packed
-// pair (x0, x1) the dot products with (1, 1) and (1, -1) give x0+x1 and x0-x1.
-__device__ __forceinline__ void widen_bf16x8_stage0(const uint4 u, float (&v)[8]) {
-  constexpr unsigned kPlusPlus = 0x3F803F80u, kPlusMinus = 0xBF803F80u;
-  v[0] = dot2_bf16(u.x, kPlusPlus, 0.0f); v[1] = dot2_bf16(u.x, kPlusMinus, 0.0f);
-  v[2] = dot2_bf16(u.y, kPlusPlus, 0.0f); v[3] = dot2_bf16(u.y, kPlusMinus, 0.0f);
-  v[4] = dot2_bf16(u.z, kPlusPlus, 0.0f); v[5] = dot2_bf16(u.z, kPlusMinus, 0.0f);
-  v[6] = dot2_bf16(u.w, kPlusPlus, 0.0f); v[7] = dot2_bf16(u.w, kPlusMinus, 0.0f);
 }
 
 // Butterflies on index bits [lo, 3) inside one 8-value chunk.
@@ -183,11 +165,6 @@ __device__ __forceinline__ void fwht_across_quad(float (&v)[NA][8], float c1, fl
     for (int j = 0; j < 8; ++j) v[a][j] = fmaf(dpp<kQuadXor2>(v[a][j]), c2, v[a][j]);
 }
 
-__device__ __forceinline__ float quad_sum(float v) {
-  v += dpp<kQuadXor1>(v);
-  return v + dpp<kQuadXor2>(v);
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -213,16 +190,6 @@ __device__ __forceinline__ float workgroup_max(float v, float* red) {
 // value.  Both compress passes evaluate it identically.
 __device__ __forceinline__ float ash_scale(float ss, float sqrt_eb) {
   return ss > 0.0f ? sqrt_eb * __builtin_amdgcn_rsqf(ss) : 1.0f;
-}
-
-// 8 values * c -> 8 E4M3FN codes (native gfx950 conversion, round to nearest
-// even).  |v*c| never exceeds 448 by more than a few ulps, which rounds to 448.
-__device__ __forceinline__ uint2 to_fp8x8(const float (&v)[8], float c) {
-  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * c, v[1] * c, 0, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * c, v[3] * c, lo, true);
-  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] * c, v[5] * c, 0, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] * c, v[7] * c, hi, true);
-  return make_uint2(static_cast<unsigned>(lo), static_cast<unsigned>(hi));
 }
 
 // 8 E4M3FN codes -> fp32 (exact).
@@ -287,36 +254,6 @@ __device__ __forceinline__ void lds_store_tile_to_global(const char* lds, uint4*
   }
 }
 
-// Lane-linear load of a tile (branch-free: chunks of rows past the end of the
-// tensor are read from the tile's last valid row instead).
-template <int ROW>
-__device__ __forceinline__ void load_tile_regs(const uint4* __restrict__ g, int64_t tile, int rows_valid,
-                                               uint4 (&v)[(kTileBlocks * ROW / 16 + 63) / 64]) {
-  constexpr int kChunksPerRow = ROW / 16, kChunks = kTileBlocks * kChunksPerRow;
-  const int lane = threadIdx.x & 63;
-  const uint4* base = g + tile * kChunks;
-#pragma unroll
-  for (int i = 0; i < (kChunks + 63) / 64; ++i) {
-    int c = 64 * i + lane;
-    if (kChunks % 64 != 0 && c >= kChunks) c = kChunks - 1;
-    const int r = c / kChunksPerRow;
-    v[i] = base[(r < rows_valid ? r : rows_valid - 1) * kChunksPerRow + c % kChunksPerRow];
-  }
-}
-
-template <int ROW, int STRIDE>
-__device__ __forceinline__ void regs_to_lds_tile(const uint4 (&v)[(kTileBlocks * ROW / 16 + 63) / 64],
-                                                 char* lds) {
-  constexpr int kChunksPerRow = ROW / 16, kChunks = kTileBlocks * kChunksPerRow;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < (kChunks + 63) / 64; ++i) {
-    const int c = 64 * i + lane;
-    if (c < kChunks)
-      *reinterpret_cast<uint4*>(lds + (c / kChunksPerRow) * STRIDE + 16 * (c % kChunksPerRow)) = v[i];
-  }
-}
-
 __device__ __forceinline__ int rows_valid(int64_t tile, int64_t nblocks) {
   const int64_t r = nblocks - tile * kTileBlocks;
   return r >= kTileBlocks ? kTileBlocks : static_cast<int>(r);
@@ -346,108 +283,6 @@ struct Quad {
     debt = c1 * c2;
   }
 };
-
-// ============================================================== VALU engine
-
-// Full Hadamard transform of this lane's bf16 chunks (times the lane's sign
-// debt) and the block's sum of squares (identical in the four lanes of the quad).
-template <int B>
-__device__ __forceinline__ float rotate_bf16(const uint4 (&raw)[Blk<B>::NA], float (&v)[Blk<B>::NA][8],
-                                             const Quad& qd) {
-  constexpr int NA = Blk<B>::NA;
-  const float ss = quad_sum(sum_squares_bf16<NA>(raw));
-#pragma unroll
-  for (int a = 0; a < NA; ++a) {
-    widen_bf16x8_stage0(raw[a], v[a]);
-    fwht_chunk<2>(v[a]);
-  }
-  fwht_across_chunks<NA>(v);
-  fwht_across_quad<NA>(v, qd.c1, qd.c2);
-  return ss;
-}
-
-template <int B, int U>
-__device__ __forceinline__ void load_x_quad(const uint4* __restrict__ x, const Walk& w, int64_t j0,
-                                            bool reverse, int64_t nblocks, const Quad& qd,
-                                            uint4 (&raw)[U][Blk<B>::NA]) {
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const bool in = j0 + u < w.count;
-    const int64_t t = in ? w.tile(j0 + u, reverse) : w.tile(0, reverse);
-    const int rv = rows_valid(t, nblocks);
-    const int64_t k = t * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1);
-#pragma unroll
-    for (int a = 0; a < Blk<B>::NA; ++a) raw[u][a] = x[k * Blk<B>::C16 + 4 * a + qd.ql];
-  }
-}
-
-// Compress, statistics pass (quad layout): alpha of every block, and per
-// workgroup the max over its blocks of alpha_k * max|H x_k| / sqrt(B).
-template <int B, int U, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void compress_stats_valu_kernel(
-    const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb,
-    float* __restrict__ alpha, float* __restrict__ partial) {
-  constexpr int NA = Blk<B>::NA;
-  __shared__ float red[WAVES];
-  const Quad qd;
-  const Walk w(WAVES, nblocks);
-  float amax = 0.0f;
-  for (int64_t j0 = 0; j0 < w.count; j0 += U) {
-    uint4 raw[U][NA];
-    load_x_quad<B, U>(x, w, j0, false, nblocks, qd, raw);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool in = j0 + u < w.count;
-      const int64_t k = (in ? w.tile(j0 + u, false) : 0) * kTileBlocks + qd.blk;
-      float v[NA][8];
-      const float a = ash_scale(rotate_bf16<B>(raw[u], v, qd), sqrt_eb);
-      if (in && k < nblocks && qd.ql == 0) alpha[k] = a;
-      float m = 0.0f;
-#pragma unroll
-      for (int c = 0; c < NA; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; j += 2) m = fmaxf(fmaxf(m, fabsf(v[c][j])), fabsf(v[c][j + 1]));
-      if (in && k < nblocks) amax = fmaxf(amax, m * (a * Blk<B>::rsqrt_b));
-    }
-  }
-  const float wg = workgroup_max<WAVES>(amax, red);
-  if (threadIdx.x == 0) partial[blockIdx.x] = wg;
-}
-
-// Compress, quantisation pass (quad layout).
-template <int B, int U, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void compress_quant_valu_kernel(
-    const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb,
-    const float* __restrict__ partial, int npartial, float* __restrict__ scale,
-    uint4* __restrict__ q) {
-  constexpr int NA = Blk<B>::NA, SROW = Blk<B>::kCodeRowQuad;
-  __shared__ __attribute__((aligned(16))) char lds_all[WAVES][kTileBlocks * SROW];
-  char* lds = lds_all[threadIdx.x >> 6];
-  const Quad qd;
-  const Walk w(WAVES, nblocks);
-  uint4 raw[U][NA];
-  if (w.count > 0) load_x_quad<B, U>(x, w, 0, true, nblocks, qd, raw);
-  const float A = wave_max_of(partial, npartial);
-  const float s = A > 0.0f ? kQmax / A : 1.0f;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
-  for (int64_t j0 = 0; j0 < w.count; j0 += U) {
-    if (j0 > 0) load_x_quad<B, U>(x, w, j0, true, nblocks, qd, raw);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (j0 + u >= w.count) break;
-      const int64_t t = w.tile(j0 + u, true);
-      float v[NA][8];
-      const float a = ash_scale(rotate_bf16<B>(raw[u], v, qd), sqrt_eb);
-      const float c = ((a * s) * Blk<B>::rsqrt_b) * qd.debt;
-#pragma unroll
-      for (int ch = 0; ch < NA; ++ch)
-        *reinterpret_cast<uint2*>(lds + qd.blk * SROW + 32 * ch + 8 * qd.ql) = to_fp8x8(v[ch], c);
-      __builtin_amdgcn_wave_barrier();
-      lds_store_tile_to_global<B, SROW>(lds, q, t, rows_valid(t, nblocks));
-      __builtin_amdgcn_wave_barrier();
-    }
-  }
-}
 
 // ============================================================== MFMA engine
 //
@@ -644,134 +479,205 @@ __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
 
 // ============================================================== fused compress
 //
-// One kernel for the whole compression when the tensor fits on chip: every
-// wavefront keeps its TPW tiles of raw bf16 x in VGPRs (they are the MFMA B
-// operands), computes alpha and its part of max|y|, meets every other
-// workgroup at a grid-wide barrier that also yields the tensor-wide max, and
-// then rotates again from registers, quantises and stores.  x is read from HBM
-// once and the codes are written once, the single fused pass the pages
-// describe [TACO pt-summary, 2.B.3].
+// One kernel for the whole compression when the tensor fits on chip.  Every
+// wavefront loads its TPW tiles of raw bf16 x, computes alpha and the rotated
+// blocks y = H x on the matrix cores, keeps y (HOLD_Y) or x (otherwise) in
+// VGPRs, and contributes to a grid-wide max of alpha |y| / sqrt(B).  After a
+// grid-wide barrier that yields that max, it scales, converts and stores its
+// codes straight from registers (recomputing y from x when only x is held).
+// x is read from HBM once and the codes are written once, the single fused
+// pass the pages describe [TACO pt-summary, 2.B.3].
 //
 // Grid barrier.  The launch makes every workgroup resident at once (grid <=
 // occupancy x CUs).  The only value exchanged is the max, so the barrier is
 // built from device-scope atomics alone, with no fences (a device-scope
-// release or acquire would write back or invalidate the whole L2):
-//   Bar {count, gen, maxbits[2], timed_out}, zero at allocation.
-//   Each workgroup reads gen (it cannot change before this workgroup
-//   arrives), folds its max into maxbits[gen & 1] (non-negative floats order
-//   like their bit patterns), and only after that atomic has returned adds 1
-//   to count.  The workgroup that brings count to G resets count and
-//   maxbits[(gen + 1) & 1] for the next call and then advances gen; the others
-//   spin on gen.  Everyone then reads maxbits[gen & 1].
-// The spin is bounded: after kSpinLimit polls it records timed_out and goes
-// on (the result is then unspecified, but every wavefront finishes).
+// release or acquire would write back or invalidate the whole L2).  Atomics
+// on one address serialise at the memory side, so the workgroups are grouped
+// into leaves of kLeafWgs, each leaf on its own 256-byte line:
+//   leaf line {count, maxbits[2], rel}: rel = (generation << 32) | max bits.
+//   root line {count, timed_out}.
+// Wavefront 0 of each workgroup reads its leaf's rel at kernel start (the
+// generation cannot change before this workgroup arrives).  Lane 0 folds the
+// workgroup max into maxbits[gen & 1] of its leaf (non-negative floats order
+// like their bit patterns), and only after that atomic has returned adds 1 to
+// the leaf count.  The workgroup that completes its leaf resets the leaf
+// count and adds 1 to the root count; the one that completes the root resets
+// it, reads every leaf's max in parallel (one lane per leaf), and writes
+// rel = (gen + 1, max) and clears maxbits[(gen + 1) & 1] on every leaf line of
+// the workspace, used or not, so that all leaves always hold the same
+// generation whatever the grid of the previous call.  Everyone else polls its
+// own leaf's rel.  The poll is bounded: after kSpinLimit polls it records
+// timed_out and goes on (the result is then unspecified, but every wavefront
+// finishes).
 
-struct Bar {
+constexpr int kLine = 256;               // bytes per barrier line
+constexpr int kLeafWgs = 16;             // workgroups per leaf
+constexpr int kLeaves = 64;              // leaf lines => at most 1024 fused workgroups
+constexpr size_t kPartialOffset = static_cast<size_t>(kLine) * (1 + kLeaves);
+constexpr unsigned kSpinLimit = 1u << 22;
+
+struct RootLine {
   unsigned count;
-  unsigned gen;
-  unsigned maxbits[2];
   unsigned timed_out;
 };
 
-constexpr unsigned kSpinLimit = 1u << 22;
+struct LeafLine {
+  unsigned count;
+  unsigned maxbits[2];
+  unsigned pad;
+  unsigned long long rel;
+};
 
-__device__ __forceinline__ float grid_max(float wg_max, Bar* __restrict__ bar, float* sh) {
-  if (threadIdx.x == 0) {
-    const unsigned gen0 = __hip_atomic_load(&bar->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned slot = gen0 & 1;
-    const unsigned prev = __hip_atomic_fetch_max(&bar->maxbits[slot], __float_as_uint(wg_max),
+__device__ __forceinline__ LeafLine* leaf_line(char* ws, unsigned l) {
+  return reinterpret_cast<LeafLine*>(ws + kLine * (1 + l));
+}
+
+template <typename T>
+__device__ __forceinline__ T load_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Release word of this workgroup's leaf, read at kernel start by wavefront 0.
+__device__ __forceinline__ unsigned long long leaf_release_word(char* ws) {
+  return load_agent(&leaf_line(ws, blockIdx.x / kLeafWgs)->rel);
+}
+
+// Grid-wide max; called by the 64 lanes of wavefront 0 with the workgroup's
+// max (uniform) and the leaf's release word from kernel start.  Every lane
+// returns the tensor-wide max.
+__device__ float grid_max_wave0(float wg_max, char* __restrict__ ws, unsigned long long rel0) {
+  const int lane = threadIdx.x & 63;
+  RootLine* root = reinterpret_cast<RootLine*>(ws);
+  const unsigned l = blockIdx.x / kLeafWgs;
+  const unsigned nleaves = (gridDim.x + kLeafWgs - 1) / kLeafWgs;
+  const unsigned in_leaf = min(static_cast<unsigned>(kLeafWgs), gridDim.x - l * kLeafWgs);
+  LeafLine* lf = leaf_line(ws, l);
+  const unsigned gen0 = static_cast<unsigned>(rel0 >> 32), slot = gen0 & 1;
+  unsigned role = 0;   // 0: wait for the release; 2: complete the barrier
+  if (lane == 0) {
+    const unsigned prev = __hip_atomic_fetch_max(&lf->maxbits[slot], __float_as_uint(wg_max),
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // prev is a finite float pattern, never ~0u: the add cannot be issued
     // before the max has returned.
     const unsigned inc = prev == ~0u ? 2u : 1u;
-    const unsigned arrived = __hip_atomic_fetch_add(&bar->count, inc, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT) + 1;
-    if (arrived == gridDim.x) {
-      __hip_atomic_store(&bar->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&bar->maxbits[slot ^ 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&bar->gen, gen0 + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      unsigned spins = 0;
-      while (__hip_atomic_load(&bar->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gen0) {
-        if (++spins == kSpinLimit) {
-          __hip_atomic_store(&bar->timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
+    if (__hip_atomic_fetch_add(&lf->count, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+        in_leaf) {
+      store_agent(&lf->count, 0u);
+      if (__hip_atomic_fetch_add(&root->count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
+          nleaves) {
+        store_agent(&root->count, 0u);
+        role = 2;
       }
     }
-    *sh = __uint_as_float(__hip_atomic_load(&bar->maxbits[slot], __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT));
   }
-  __syncthreads();
-  return *sh;
-}
-
-template <int B>
-__device__ __forceinline__ void quant_tile_mfma_c(const HadFrag& F, const uint4 (&xr)[B / 32], int64_t t,
-                                                  int64_t nblocks, float c, char* lds,
-                                                  uint4* __restrict__ q) {
-  constexpr int SROW = Blk<B>::kCodeRowMfma;
-  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  role = __builtin_amdgcn_readfirstlane(role);
+  if (role == 2) {
+    unsigned mx = 0;
+    if (lane < static_cast<int>(nleaves)) mx = load_agent(&leaf_line(ws, lane)->maxbits[slot]);
 #pragma unroll
-  for (int mt = 0; mt < B / 16; ++mt) {
-    const f32x4_t y = hadamard_mtile<B>(F, xr, mt);
-    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * c, y[1] * c, 0, false);
-    wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * c, y[3] * c, wd, true);
-    *reinterpret_cast<int*>(lds + n * SROW + 16 * mt + 4 * g) = wd;
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, static_cast<unsigned>(__shfl_xor(static_cast<int>(mx), o)));
+    const unsigned long long rel = (static_cast<unsigned long long>(gen0 + 1) << 32) | mx;
+    LeafLine* o = leaf_line(ws, lane);          // kLeaves == 64: one leaf per lane
+    store_agent(&o->maxbits[slot ^ 1], 0u);
+    store_agent(&o->rel, rel);
+    return __uint_as_float(mx);
   }
-  __builtin_amdgcn_wave_barrier();
-  lds_store_tile_to_global<B, SROW>(lds, q, t, rows_valid(t, nblocks));
-  __builtin_amdgcn_wave_barrier();
+  unsigned long long r = 0;
+  if (lane == 0) {
+    unsigned spins = 0;
+    while (static_cast<unsigned>((r = load_agent(&lf->rel)) >> 32) == gen0) {
+      if (++spins == kSpinLimit) {
+        store_agent(&root->timed_out, 1u);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  return __uint_as_float(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(r)));
+}
+static_assert(kLeaves == 64, "grid_max_wave0 releases one leaf per lane");
+
+// Codes of rows 16 mt .. 16 mt + 15 of a tile's rotated blocks (MFMA C
+// layout): scale by c, convert, and place them in the wavefront's LDS tile.
+template <int B>
+__device__ __forceinline__ void codes_to_lds_mfma(const f32x4_t y, float c, int mt, char* lds) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  int wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * c, y[1] * c, 0, false);
+  wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * c, y[3] * c, wd, true);
+  *reinterpret_cast<int*>(lds + n * Blk<B>::kCodeRowMfma + 16 * mt + 4 * g) = wd;
 }
 
 // Wavefront w of W owns tiles w, w + W, ..., w + (TPW-1) W (those < ntiles).
-template <int B, int TPW>
-__global__ __launch_bounds__(kThreads) void compress_fused_kernel(
+template <int B, int TPW, bool HOLD_Y, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
     const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
-    float* __restrict__ scale, Bar* __restrict__ bar, uint4* __restrict__ q) {
-  constexpr int NK = B / 32, SROW = Blk<B>::kCodeRowMfma;
-  __shared__ float red[kWaves];
+    float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q) {
+  constexpr int NK = B / 32, NM = B / 16, SROW = Blk<B>::kCodeRowMfma;
+  __shared__ float red[WAVES];
   __shared__ float amax_sh;
-  __shared__ __attribute__((aligned(16))) char lds_all[kWaves][kTileBlocks * SROW];
+  __shared__ __attribute__((aligned(16))) char lds_all[WAVES][kTileBlocks * SROW];
   char* lds = lds_all[threadIdx.x >> 6];
   const HadFrag F = make_hadamard_fragments();
   const int lane = threadIdx.x & 63, n = lane & 15;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
-  const int64_t wid = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + (threadIdx.x >> 6);
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
+  unsigned long long rel0 = 0;
+  if (threadIdx.x < 64) rel0 = leaf_release_word(ws);
   uint4 xr[TPW][NK];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int64_t t = wid + i * nw;
     load_tile_mfma<B>(x, t < ntiles ? t : ntiles - 1, nblocks, xr[i]);
   }
+  f32x4_t y[HOLD_Y ? TPW : 1][NM];
   float al[TPW];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int64_t t = wid + i * nw;
+    const int rv = rows_valid(t < ntiles ? t : ntiles - 1, nblocks);
     al[i] = ash_scale(column_sum_squares<B>(xr[i]), sqrt_eb);
-    if (t < ntiles) {
-      const int rv = rows_valid(t, nblocks);
-      alpha[t * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
-      float m = 0.0f;
+    if (t < ntiles) alpha[t * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
+    float m = 0.0f;
 #pragma unroll
-      for (int mt = 0; mt < B / 16; ++mt) {
-        const f32x4_t y = hadamard_mtile<B>(F, xr[i], mt);
-        m = fmaxf(fmaxf(m, fabsf(y[0])), fabsf(y[1]));
-        m = fmaxf(fmaxf(m, fabsf(y[2])), fabsf(y[3]));
-      }
-      if (n < rv) amax = fmaxf(amax, m * (al[i] * Blk<B>::rsqrt_b));
+    for (int mt = 0; mt < NM; ++mt) {
+      const f32x4_t v = hadamard_mtile<B>(F, xr[i], mt);
+      if (HOLD_Y) y[HOLD_Y ? i : 0][mt] = v;
+      m = fmaxf(fmaxf(m, fabsf(v[0])), fabsf(v[1]));
+      m = fmaxf(fmaxf(m, fabsf(v[2])), fabsf(v[3]));
     }
+    if (t < ntiles && n < rv) amax = fmaxf(amax, m * (al[i] * Blk<B>::rsqrt_b));
   }
-  const float A = grid_max(workgroup_max<kWaves>(amax, red), bar, &amax_sh);
+  const float wg = workgroup_max<WAVES>(amax, red);
+  if (threadIdx.x < 64) {
+    const float A = grid_max_wave0(wg, ws, rel0);
+    if (threadIdx.x == 0) amax_sh = A;
+  }
+  __syncthreads();
+  const float A = amax_sh;
   const float s = A > 0.0f ? kQmax / A : 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int64_t t = wid + i * nw;
-    if (t < ntiles) quant_tile_mfma_c<B>(F, xr[i], t, nblocks, (al[i] * s) * Blk<B>::rsqrt_b, lds, q);
+    if (t >= ntiles) continue;
+    const float c = (al[i] * s) * Blk<B>::rsqrt_b;
+    if (HOLD_Y) {
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) codes_to_lds_mfma<B>(y[HOLD_Y ? i : 0][mt], c, mt, lds);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) codes_to_lds_mfma<B>(hadamard_mtile<B>(F, xr[i], mt), c, mt, lds);
+    }
+    __builtin_amdgcn_wave_barrier();
+    lds_store_tile_to_global<B, SROW>(lds, q, t, rows_valid(t, nblocks));
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -786,61 +692,48 @@ __device__ __forceinline__ void rotate_f32(float (&v)[NA][8], const Quad& qd) {
   fwht_across_quad<NA>(v, qd.c1, qd.c2);
 }
 
-// A tile's FP8 codes: lane-linear loads (kept in registers until needed).
-template <int B>
-using CodeRegs = uint4[(kTileBlocks * B / 16 + 63) / 64];
-
-// Decompress one tile whose codes (lane-linear) and alpha are in registers.
-// The wavefront's LDS tile holds first the codes, then the bf16 output.
-template <int B>
-__device__ __forceinline__ void decompress_tile(const CodeRegs<B>& cr, float al, float s, int64_t t,
-                                                int64_t nblocks, const Quad& qd, char* lds,
-                                                uint4* __restrict__ out) {
-  constexpr int NA = Blk<B>::NA, CROW = Blk<B>::kCodeRowQuad, OROW = Blk<B>::kBf16RowQuad;
-  regs_to_lds_tile<B, CROW>(cr, lds);
-  __builtin_amdgcn_wave_barrier();
-  float v[NA][8];
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-    from_fp8x8(*reinterpret_cast<const uint2*>(lds + qd.blk * CROW + 32 * a + 8 * qd.ql), v[a]);
-  __builtin_amdgcn_wave_barrier();
-  rotate_f32<NA>(v, qd);
-  const float r = (Blk<B>::rsqrt_b / (al * s)) * qd.debt;
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-    *reinterpret_cast<uint4*>(lds + qd.blk * OROW + 64 * a + 16 * qd.ql) = to_bf16x8(v[a], r);
-  __builtin_amdgcn_wave_barrier();
-  lds_store_tile_to_global<2 * B, OROW>(lds, out, t, rows_valid(t, nblocks));
-  __builtin_amdgcn_wave_barrier();
-}
-
-template <int B>
-__device__ __forceinline__ void load_codes_tile(const uint4* __restrict__ q, const float* __restrict__ alpha,
-                                                int64_t t, int64_t nblocks, const Quad& qd,
-                                                CodeRegs<B>& cr, float& al) {
-  const int rv = rows_valid(t, nblocks);
-  load_tile_regs<B>(q, t, rv, cr);
-  al = alpha[t * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1)];
-}
-
 // Decompress: decode, rotate, multiply by 1/(alpha_k s sqrt(B)), round to
-// bf16.  Persistent, software-pipelined two tiles deep.
-template <int B>
+// bf16.  Global accesses are direct, in the quad layout: one load instruction
+// moves 32 contiguous bytes of codes per quad, one store 64 contiguous bytes
+// of bf16 (staging through LDS measured slower here).  Each wavefront first
+// issues the loads of all U of its tiles, then decodes, rotates and stores.
+template <int B, int U>
 __global__ __launch_bounds__(kThreads) void decompress_kernel(
-    const uint4* __restrict__ q, const float* __restrict__ alpha,
-    const float* __restrict__ scale, int64_t nblocks, uint4* __restrict__ out) {
-  constexpr int OROW = Blk<B>::kBf16RowQuad;
-  __shared__ __attribute__((aligned(16))) char lds_all[kWaves][kTileBlocks * OROW];
-  char* lds = lds_all[threadIdx.x >> 6];
+    const uint2* __restrict__ q, const float* __restrict__ alpha, const float* __restrict__ scale,
+    int64_t nblocks, uint4* __restrict__ out) {
+  constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16;
   const Quad qd;
-  const Walk w(kWaves, nblocks);
   const float s = *scale;
-  struct Buf { CodeRegs<B> c; float al; } xa_, xb_;
-#define LOAD(buf, j) load_codes_tile<B>(q, alpha, w.tile(j, false), nblocks, qd, buf.c, buf.al)
-#define WORK(buf, j) decompress_tile<B>(buf.c, buf.al, s, w.tile(j, false), nblocks, qd, lds, out)
-  TACO_PIPELINE_2(w.count, LOAD, WORK);
-#undef LOAD
-#undef WORK
+  const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
+  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
+       t0 += W * U) {
+    uint2 raw[U][NA];
+    float al[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = (t0 + u * W) * kTileBlocks + qd.blk;
+      const bool ok = t0 + u * W < ntiles && k < nblocks;
+#pragma unroll
+      for (int a = 0; a < NA; ++a) raw[u][a] = ok ? q[k * C16 + 4 * a + qd.ql] : make_uint2(0, 0);
+      al[u] = ok ? alpha[k] : 1.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = (t0 + u * W) * kTileBlocks + qd.blk;
+      const bool ok = t0 + u * W < ntiles && k < nblocks;
+      float v[NA][8];
+#pragma unroll
+      for (int a = 0; a < NA; ++a) from_fp8x8(raw[u][a], v[a]);
+      rotate_f32<NA>(v, qd);
+      const float r = (Blk<B>::rsqrt_b / (al[u] * s)) * qd.debt;
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        const uint4 o = to_bf16x8(v[a], r);
+        if (ok) out[k * C16 + 4 * a + qd.ql] = o;
+      }
+    }
+  }
 }
 
 struct Parts {
@@ -852,66 +745,68 @@ struct Parts {
 // Decompress-and-sum.  The rotation is linear, so the parts are combined
 // before it: acc = sum_p decode(q_p) / (alpha_{p,k} s_p), then one rotation
 // and the 1/sqrt(B) factor.  This is the same sum as decompressing each part
-// and adding the results, with P-1 fewer transforms per block.  The number of
-// parts is a template argument so that exactly P tiles of codes are in flight
-// (all loaded before any is used).
-template <int B, int P>
+// and adding the results, with P-1 fewer transforms per block.  Global
+// accesses as in decompress_kernel; the codes of all P parts of U tiles are
+// loaded before any is used.
+template <int B, int P, int U>
 __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
     Parts parts, int64_t nblocks, uint4* __restrict__ out) {
-  constexpr int NA = Blk<B>::NA, CROW = Blk<B>::kCodeRowQuad, OROW = Blk<B>::kBf16RowQuad;
-  __shared__ __attribute__((aligned(16))) char lds_all[kWaves][kTileBlocks * OROW];
-  char* lds = lds_all[threadIdx.x >> 6];
+  constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16;
   const Quad qd;
-  const Walk w(kWaves, nblocks);
   float s[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) s[p] = *parts.scale[p];
-  for (int64_t j = 0; j < w.count; ++j) {
-    const int64_t t = w.tile(j, false);
-    const int rv = rows_valid(t, nblocks);
-    CodeRegs<B> cr[P];
-    float wt[P];
+  const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
+  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
+       t0 += W * U) {
+    uint2 raw[U][P][NA];
+    float wt[U][P];
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      load_tile_regs<B>(parts.q[p], t, rv, cr[p]);
-      wt[p] = parts.alpha[p][t * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1)];
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = (t0 + u * W) * kTileBlocks + qd.blk;
+      const bool ok = t0 + u * W < ntiles && k < nblocks;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const uint2* qp = reinterpret_cast<const uint2*>(parts.q[p]);
+#pragma unroll
+        for (int a = 0; a < NA; ++a) raw[u][p][a] = ok ? qp[k * C16 + 4 * a + qd.ql] : make_uint2(0, 0);
+        wt[u][p] = ok ? parts.alpha[p][k] : 1.0f;
+      }
     }
-    float acc[NA][8];
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = (t0 + u * W) * kTileBlocks + qd.blk;
+      const bool ok = t0 + u * W < ntiles && k < nblocks;
+      float acc[NA][8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) acc[a][jj] = 0.0f;
+      for (int a = 0; a < NA; ++a)
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      regs_to_lds_tile<B, CROW>(cr[p], lds);
-      __builtin_amdgcn_wave_barrier();
-      const float wp = 1.0f / (wt[p] * s[p]);
+        for (int j = 0; j < 8; ++j) acc[a][j] = 0.0f;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const float wp = 1.0f / (wt[u][p] * s[p]);
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+          float d[8];
+          from_fp8x8(raw[u][p][a], d);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[a][j] = fmaf(d[j], wp, acc[a][j]);
+        }
+      }
+      rotate_f32<NA>(acc, qd);
+      const float r = Blk<B>::rsqrt_b * qd.debt;
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
-        float d[8];
-        from_fp8x8(*reinterpret_cast<const uint2*>(lds + qd.blk * CROW + 32 * a + 8 * qd.ql), d);
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) acc[a][jj] = fmaf(d[jj], wp, acc[a][jj]);
+        const uint4 o = to_bf16x8(acc[a], r);
+        if (ok) out[k * C16 + 4 * a + qd.ql] = o;
       }
-      __builtin_amdgcn_wave_barrier();
     }
-    rotate_f32<NA>(acc, qd);
-    const float r = Blk<B>::rsqrt_b * qd.debt;
-#pragma unroll
-    for (int a = 0; a < NA; ++a)
-      *reinterpret_cast<uint4*>(lds + qd.blk * OROW + 64 * a + 16 * qd.ql) = to_bf16x8(acc[a], r);
-    __builtin_amdgcn_wave_barrier();
-    lds_store_tile_to_global<2 * B, OROW>(lds, out, t, rv);
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
 // ----------------------------------------------------------------- host side
 
-// The VALU compress engine holds a whole transformed tile in registers and
-// keeps one tile in flight; it uses 512-thread workgroups (<= 256 VGPRs).
-constexpr int kUnrollCompressValu = 1;
-constexpr int kWavesValu = 8;
 // Persistent kernels aim for at least this many tiles per wavefront (so the
 // software pipeline has something to overlap) but never fewer wavefronts than
 // min(tiles, 4 per CU).
@@ -944,15 +839,12 @@ taco_status_t check_shape(int64_t tokens, int64_t hidden, int32_t block) {
   return TACO_OK;
 }
 
-// Workgroups for walking ceil(nblocks/16) tiles with `waves` wavefronts per
-// workgroup and `unroll` tiles per wavefront per trip, capped at `cap`.
-int grid_for(int64_t nblocks, int waves, int unroll, int cap) {
+// Workgroups of one-tile-per-wavefront kernels (the grid-stride loops cover
+// any tiles beyond).
+int tile_grid(int64_t nblocks) {
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
-  const int64_t per_wg = static_cast<int64_t>(waves) * unroll;
-  int64_t g = (tiles + per_wg - 1) / per_wg;
-  if (g > cap) g = cap;
-  if (g < 1) g = 1;
-  return static_cast<int>(g);
+  const int64_t g = (tiles + kWaves - 1) / kWaves;
+  return static_cast<int>(std::min<int64_t>(std::max<int64_t>(g, 1), INT32_MAX));
 }
 
 // Workgroups of `kernel` that fit on the whole device at once.
@@ -983,24 +875,36 @@ int persistent_grid(int64_t nblocks, int waves, int resident_wgs) {
   return static_cast<int>(g);
 }
 
-// Resident wavefronts of the fused kernel for TPW tiles per wavefront.
-template <int B, int TPW>
-int64_t fused_capacity() {
-  static const int wgs = resident_grid(compress_fused_kernel<B, TPW>, kThreads);
-  return static_cast<int64_t>(wgs) * kWaves;
-}
-
-template <int B, int TPW>
-bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, Bar* bar,
+// Launches the fused compress with TPW tiles per wavefront if every one of its
+// wavefronts can be resident at once (and the barrier has leaves for them).
+template <int B, int TPW, bool HOLD_Y, int WAVES>
+bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, char* ws,
                uint4* q, hipStream_t stream) {
+  static const int cap = std::min(resident_grid(compress_fused_kernel<B, TPW, HOLD_Y, WAVES>, 64 * WAVES),
+                                  kLeaves * kLeafWgs);
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
-  const int64_t waves = (tiles + TPW - 1) / TPW;
-  if (waves > fused_capacity<B, TPW>()) return false;
-  const int g = static_cast<int>((waves + kWaves - 1) / kWaves);
-  hipLaunchKernelGGL((compress_fused_kernel<B, TPW>), dim3(g), dim3(kThreads), 0, stream,
-                     x, nblocks, sqrt_eb, alpha, scale, bar, q);
+  const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
+  if (g > cap) return false;
+  hipLaunchKernelGGL((compress_fused_kernel<B, TPW, HOLD_Y, WAVES>), dim3(g), dim3(64 * WAVES), 0,
+                     stream, x, nblocks, sqrt_eb, alpha, scale, ws, q);
   return true;
 }
+
+// Fused configurations, fewest tiles per wavefront first; the rotated blocks
+// take at most 64 of the 128 VGPRs a lane has at 16 wavefronts per CU.
+// Larger tensors (beyond 64 MiB of fp32 y) take the two-pass path.
+template <int B>
+bool launch_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, char* ws,
+                  uint4* q, hipStream_t stream) {
+  if (try_fused<B, 1, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream)) return true;
+  if constexpr (B <= 128)
+    if (try_fused<B, 2, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream)) return true;
+  if constexpr (B == 64)
+    if (try_fused<B, 4, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream)) return true;
+  return false;
+}
+
+bool g_single_pass = true;   // fused compress when the tensor fits (process-wide)
 
 template <int B>
 void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, float* alpha,
@@ -1008,49 +912,31 @@ void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, f
   const float sqrt_eb = static_cast<float>(sqrt(static_cast<double>(energy) * B));
   const uint4* xv = static_cast<const uint4*>(x);
   uint4* qv = reinterpret_cast<uint4*>(q);
-  Bar* bar = static_cast<Bar*>(workspace);
-  float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kWorkspaceHeader);
-  if (g_engine != TACO_ENGINE_VALU) {
-    // Single fused pass when the tensor fits in the resident wavefronts' VGPRs.
-    if (try_fused<B, 1>(xv, nblocks, sqrt_eb, alpha, scale, bar, qv, stream)) return;
-    if (try_fused<B, 2>(xv, nblocks, sqrt_eb, alpha, scale, bar, qv, stream)) return;
-    if (try_fused<B, 4>(xv, nblocks, sqrt_eb, alpha, scale, bar, qv, stream)) return;
-    if (B <= 128 && try_fused<B, 8>(xv, nblocks, sqrt_eb, alpha, scale, bar, qv, stream)) return;
-    static const int cap = std::min(resident_grid(compress_stats_mfma_kernel<B>, kThreads),
-                                    resident_grid(compress_quant_mfma_kernel<B>, kThreads));
-    const int g = persistent_grid(nblocks, kWaves, std::min(cap, kMaxPartials));
-    hipLaunchKernelGGL((compress_stats_mfma_kernel<B>), dim3(g), dim3(kThreads), 0, stream,
-                       xv, nblocks, sqrt_eb, alpha, partial);
-    hipLaunchKernelGGL((compress_quant_mfma_kernel<B>), dim3(g), dim3(kThreads), 0, stream,
-                       xv, nblocks, sqrt_eb, partial, g, scale, qv);
-  } else {
-    constexpr int UV = kUnrollCompressValu, WV = kWavesValu;
-    static const int cap = std::min(resident_grid(compress_stats_valu_kernel<B, UV, WV>, 64 * WV),
-                                    resident_grid(compress_quant_valu_kernel<B, UV, WV>, 64 * WV));
-    const int g = grid_for(nblocks, WV, UV, std::min(cap, kMaxPartials));
-    hipLaunchKernelGGL((compress_stats_valu_kernel<B, UV, WV>), dim3(g), dim3(64 * WV), 0, stream,
-                       xv, nblocks, sqrt_eb, alpha, partial);
-    hipLaunchKernelGGL((compress_quant_valu_kernel<B, UV, WV>), dim3(g), dim3(64 * WV), 0, stream,
-                       xv, nblocks, sqrt_eb, partial, g, scale, qv);
-  }
+  char* ws = static_cast<char*>(workspace);
+  float* partial = reinterpret_cast<float*>(ws + kPartialOffset);
+  // Single fused pass when the tensor fits in the resident wavefronts' VGPRs.
+  if (g_single_pass && launch_fused<B>(xv, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
+  static const int cap = std::min(resident_grid(compress_stats_mfma_kernel<B>, kThreads),
+                                  resident_grid(compress_quant_mfma_kernel<B>, kThreads));
+  const int g = persistent_grid(nblocks, kWaves, std::min(cap, kMaxPartials));
+  hipLaunchKernelGGL((compress_stats_mfma_kernel<B>), dim3(g), dim3(kThreads), 0, stream,
+                     xv, nblocks, sqrt_eb, alpha, partial);
+  hipLaunchKernelGGL((compress_quant_mfma_kernel<B>), dim3(g), dim3(kThreads), 0, stream,
+                     xv, nblocks, sqrt_eb, partial, g, scale, qv);
 }
 
 template <int B>
 void launch_decompress(const uint8_t* q, const float* alpha, const float* scale, int64_t nblocks,
                        void* out, hipStream_t stream) {
-  static const int cap = resident_grid(decompress_kernel<B>, kThreads);
-  const int g = persistent_grid(nblocks, kWaves, cap);
-  hipLaunchKernelGGL((decompress_kernel<B>), dim3(g), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint4*>(q), alpha, scale, nblocks,
+  hipLaunchKernelGGL((decompress_kernel<B, 1>), dim3(tile_grid(nblocks)), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint2*>(q), alpha, scale, nblocks,
                      static_cast<uint4*>(out));
 }
 
 template <int B, int P>
 void launch_decompress_sum_p(const Parts& parts, int64_t nblocks, void* out, hipStream_t stream) {
-  static const int cap = resident_grid(decompress_sum_kernel<B, P>, kThreads);
-  const int g = persistent_grid(nblocks, kWaves, cap);
-  hipLaunchKernelGGL((decompress_sum_kernel<B, P>), dim3(g), dim3(kThreads), 0, stream,
-                     parts, nblocks, static_cast<uint4*>(out));
+  hipLaunchKernelGGL((decompress_sum_kernel<B, P, 1>), dim3(tile_grid(nblocks)), dim3(kThreads), 0,
+                     stream, parts, nblocks, static_cast<uint4*>(out));
 }
 
 template <int B>
@@ -1093,9 +979,9 @@ const char* taco_status_string(taco_status_t status) {
 const char* taco_version(void) { return "0.2.0"; }
 
 taco_status_t taco_set_rotation_engine(taco_engine_t engine) {
-  // The VALU engine is switched off: its compress kernels took a GPU memory
-  // fault on a 3-tile tensor whose cause has not been found (it passes a CPU
-  // build with AddressSanitizer).  Until it is, only the MFMA engine runs.
+  // The VALU compress engine has been removed: its kernels took a GPU memory
+  // fault on a 3-tile tensor whose cause was not found.  Only the MFMA engine
+  // remains.
   if (engine == TACO_ENGINE_VALU) return TACO_ERR_BAD_ENGINE;
   if (engine != TACO_ENGINE_AUTO && engine != TACO_ENGINE_MFMA) return TACO_ERR_BAD_ENGINE;
   g_engine = engine;
@@ -1104,6 +990,10 @@ taco_status_t taco_set_rotation_engine(taco_engine_t engine) {
 
 taco_engine_t taco_get_rotation_engine(void) { return static_cast<taco_engine_t>(g_engine); }
 
+void taco_set_single_pass(int enable) { g_single_pass = enable != 0; }
+
+int taco_get_single_pass(void) { return g_single_pass ? 1 : 0; }
+
 int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block) {
   if (check_shape(tokens, hidden, block) != TACO_OK) return -1;
   return tokens * (hidden / block);
@@ -1111,7 +1001,7 @@ int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block) {
 
 size_t taco_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block) {
   if (check_shape(tokens, hidden, block) != TACO_OK) return 0;
-  return kWorkspaceHeader + static_cast<size_t>(kMaxPartials) * sizeof(float);
+  return kPartialOffset + static_cast<size_t>(kMaxPartials) * sizeof(float);
 }
 
 taco_status_t taco_compress(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,

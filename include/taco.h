@@ -90,18 +90,28 @@ const char* taco_version(void);
 taco_status_t taco_set_rotation_engine(taco_engine_t engine);
 taco_engine_t taco_get_rotation_engine(void);
 
+/* Pass structure of taco_compress for the whole process.  enable != 0 (the
+ * default): one fused kernel that keeps the tensor in registers across a
+ * grid-wide max whenever every tile fits in the resident wavefronts, two
+ * kernels otherwise (statistics, then quantisation re-reading x).  enable == 0:
+ * always the two kernels.  Both give identical results. */
+void taco_set_single_pass(int enable);
+int taco_get_single_pass(void);
+
 /* Number of per-block ASH scales of a [tokens, hidden] tensor at this block
  * size (tokens * hidden / block), or -1 if the shape or block is invalid. */
 int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block);
 
 /* Bytes of device workspace taco_compress needs for this shape (0 for an
- * invalid shape).  The workspace holds the state of a grid-wide barrier and
- * per-workgroup partial maxima.  It must be zero-filled once when allocated;
- * every call leaves it ready for the next one.  Calls that share a workspace
- * must be ordered (the same stream), and while a compress runs no other
- * kernel may occupy the GPU's compute units (its workgroups must all be
- * resident at once to pass the barrier; if they are not, the barrier gives up
- * after a bounded wait and the call's result is unspecified). */
+ * invalid shape; the same 33024 bytes for every valid one).  The workspace
+ * holds the state of a grid-wide barrier and per-workgroup partial maxima.
+ * It must be zero-filled once when allocated; every call leaves it ready for
+ * the next one.  Calls that share a workspace must be ordered (the same
+ * stream).  While a single-pass compress runs no other kernel may occupy the
+ * GPU's compute units: its workgroups must all be resident at once to pass the
+ * barrier; if they are not, the barrier gives up after a bounded wait and the
+ * call's result is unspecified (taco_set_single_pass(0) removes the
+ * requirement). */
 size_t taco_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block);
 
 /*

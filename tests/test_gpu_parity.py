@@ -45,22 +45,26 @@ def gpu_triple_np(q, a, s):
 MAX_BF16_FRAC = 0.05
 
 
-ENGINES = ["mfma", pytest.param("valu", marks=pytest.mark.skip(
-    reason="VALU rotation engine disabled in libtaco: its compress kernels took a GPU memory "
-           "fault on a [3, 1024] tensor (block 64) whose cause is not yet found"))]
+# Compress paths: the fused single-pass kernel (used whenever the tensor fits
+# on chip) and the two-kernel path (larger tensors, or forced).
+ENGINES = ["fused", "two_pass", pytest.param("valu", marks=pytest.mark.skip(
+    reason="VALU rotation engine removed from libtaco: its compress kernels took a GPU memory "
+           "fault on a [3, 1024] tensor (block 64) whose cause was not found"))]
 
 
 @pytest.fixture(params=ENGINES)
 def engine(request, taco):
-    taco.set_rotation_engine(request.param)
+    taco.set_rotation_engine("valu" if request.param == "valu" else "mfma")
+    taco.set_single_pass(request.param != "two_pass")
     yield request.param
     taco.set_rotation_engine("auto")
+    taco.set_single_pass(True)
 
 
 def run_round_trip(taco, bits, block, E=1.0, max_code_frac=1e-4, max_bf16_frac=MAX_BF16_FRAC):
     T, H = bits.shape
     print(f"[case] compress/decompress shape=({T},{H}) block={block} E={E} "
-          f"engine={taco.get_rotation_engine()}", flush=True)
+          f"engine={taco.get_rotation_engine()} single_pass={taco.get_single_pass()}", flush=True)
     q_o, a_o, s_o = oracle.compress(bits, block, E)
     x = to_gpu_bits(bits)
     q_g, a_g, s_g = gpu_triple_np(*taco.compress(x, block, E))
@@ -159,6 +163,35 @@ def test_every_fp8_code_decodes_exactly(taco):
     got = oracle.bf16_bits_to_f64(W.bf16_bits(out))
     want = oracle.e4m3_decode(codes) / 8.0
     assert np.array_equal(got, np.repeat(want[:, None], 64, axis=1))
+
+
+def _compress_with(taco, x, block, single_pass, ws):
+    taco.set_single_pass(single_pass)
+    try:
+        return [t.clone() for t in taco.compress(x, block, workspace=ws)]
+    finally:
+        taco.set_single_pass(True)
+
+
+def test_fused_matches_two_pass_bitwise(taco):
+    """The fused kernel and the two-kernel path evaluate the same arithmetic:
+    identical codes, alpha and scale.  The shapes alternate between grids of
+    many barrier leaves and of one, on one workspace, so every call must find
+    the barrier state the previous call left; the barrier never times out."""
+    nbytes = taco.workspace_bytes(4096, 4096, 128)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    cases = [("gpt3_6p7b_act", 4096, 128), ("tiny", 3, 64), ("gpt2_1p5b", 4096, 64),
+             ("tiny", 256, 256), ("gpt3_6p7b_grad", 1024, 128), ("dsum_part", 17, 256),
+             ("gpt3_6p7b_act", 4096, 128)]
+    for name, tokens, block in cases:
+        print(f"[case] fused vs two-pass {name} tokens={tokens} block={block}", flush=True)
+        x = W.make(name, seed=tokens, tokens=tokens).cuda()
+        fused = _compress_with(taco, x, block, True, ws)
+        two = _compress_with(taco, x, block, False, ws)
+        for a, b in zip(fused, two):
+            assert torch.equal(a, b)
+        timed_out = int(ws[4:8].cpu().numpy().view(np.uint32)[0])
+        assert timed_out == 0
 
 
 def test_determinism(taco, engine):
