@@ -46,11 +46,16 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rotate", type=int, default=4, help="buffer sets rotated over (>= 1 GiB total)")
-    p.add_argument("--cpu-rows", type=int, default=1024,
+    p.add_argument("--cpu-rows", type=int, default=TOKENS,
                    help="rows of the workload the oracle is timed on (cpu_baseline)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="the oracle's step is repeated until at least this much CPU time")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--engine", choices=["auto", "valu", "mfma"], default=None,
-                   help="rotation engine of compress (default: the library's choice)")
+    p.add_argument("--single-pass", choices=["on", "off"], default="on",
+                   help="fused single-pass compress when the tensor fits (default) or the two-kernel path")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="before timing, run 8 plain device copies of this many MiB (a known-size "
+                        "kernel that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE in the same process)")
     return p.parse_args()
 
 
@@ -74,9 +79,9 @@ def measured_traffic():
     return c.get("traffic_bytes_per_call")
 
 
-def cpu_baseline(rows: int):
-    """The oracle, as it is, on the first `rows` rows of the same step (1 thread)."""
-    import numpy as np
+def cpu_baseline(rows: int, min_seconds: float):
+    """The oracle, as it is, on the first `rows` rows of the same step (1 BLAS
+    thread), repeated until at least `min_seconds` of CPU work."""
     from threadpoolctl import threadpool_limits
 
     import oracle
@@ -86,18 +91,23 @@ def cpu_baseline(rows: int):
     grad = W.bf16_bits(W.make("gpt3_6p7b_grad", seed=1, tokens=rows))
     parts = [oracle.compress(W.bf16_bits(W.make("gpt3_6p7b_act", seed=10 + p, tokens=rows)), BLOCK)
              for p in range(NPARTS)]
+    runs = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        for x in (act, grad):
-            q, a, s = oracle.compress(x, BLOCK)
-            oracle.decompress(q, a, s, BLOCK)
-        oracle.decompress_sum(parts, BLOCK)
-        dt = time.perf_counter() - t0
-    nbytes = 2 * rows * HIDDEN * 5          # bf16 bytes of the 5 calls
+        while True:
+            for x in (act, grad):
+                q, a, s = oracle.compress(x, BLOCK)
+                oracle.decompress(q, a, s, BLOCK)
+            oracle.decompress_sum(parts, BLOCK)
+            runs += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    nbytes = 2 * rows * HIDDEN * 5 * runs        # bf16 bytes of the 5 calls per step
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one step on rows 0..{rows - 1} of the [{TOKENS},{HIDDEN}] workload "
-                      f"({rows}x{HIDDEN} per tensor), numpy fp64, BLAS limited to 1 thread, "
-                      f"{dt:.2f} s"}
+            "sample": f"{runs} step(s) on rows 0..{rows - 1} of the [{TOKENS},{HIDDEN}] workload "
+                      f"({rows}x{HIDDEN} per tensor; the 4 decompress-sum parts compressed beforehand), "
+                      f"numpy fp64, BLAS limited to 1 thread, {dt:.1f} s"}
 
 
 def main():
@@ -142,8 +152,14 @@ def main():
     del act, grad, part_src
     ws = torch.zeros(taco.workspace_bytes(TOKENS, HIDDEN, BLOCK), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    if args.engine:
-        taco.set_rotation_engine(args.engine)
+    taco.set_single_pass(args.single_pass == "on")
+    if args.copy_probe_mib > 0:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     set_bytes = sum(t.numel() * t.element_size() for t in
                     [sets[0]["act"], sets[0]["grad"], *sets[0]["q"], *sets[0]["a"], *sets[0]["xh"],
                      sets[0]["sum"], *[t for p in sets[0]["parts"] for t in p]])
@@ -252,7 +268,8 @@ def main():
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
-            "kernel": "compress (statistics + quantisation kernels, " + taco.get_rotation_engine() + " rotation)",
+            "kernel": ("compress_fused_kernel (single pass)" if taco.get_single_pass()
+                       else "compress_stats_mfma_kernel + compress_quant_mfma_kernel"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -274,7 +291,7 @@ def main():
                   "calls over all buffer sets",
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(args.cpu_rows, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
