@@ -494,21 +494,23 @@ __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
 // release or acquire would write back or invalidate the whole L2).  Atomics
 // on one address serialise at the memory side, so the workgroups are grouped
 // into leaves of kLeafWgs, each leaf on its own 256-byte line:
-//   leaf line {count, maxbits[2], rel}: rel = (generation << 32) | max bits.
-//   root line {count, timed_out}.
-// Wavefront 0 of each workgroup reads its leaf's rel at kernel start (the
-// generation cannot change before this workgroup arrives).  Lane 0 folds the
-// workgroup max into maxbits[gen & 1] of its leaf (non-negative floats order
-// like their bit patterns), and only after that atomic has returned adds 1 to
-// the leaf count.  The workgroup that completes its leaf resets the leaf
-// count and adds 1 to the root count; the one that completes the root resets
-// it, reads every leaf's max in parallel (one lane per leaf), and writes
-// rel = (gen + 1, max) and clears maxbits[(gen + 1) & 1] on every leaf line of
-// the workspace, used or not, so that all leaves always hold the same
-// generation whatever the grid of the previous call.  Everyone else polls its
-// own leaf's rel.  The poll is bounded: after kSpinLimit polls it records
-// timed_out and goes on (the result is then unspecified, but every wavefront
-// finishes).
+//   leaf line {count (64-bit), maxbits, rel}: rel = (call + 1) << 32 | max bits
+//   root line {count (64-bit), timed_out}
+// The counts never reset: every call adds exactly kLeafWgs to every leaf and
+// kLeaves to the root (the first workgroup of a partial leaf adds the missing
+// arrivals, the first leaf adds the missing leaves, and the completing
+// workgroup advances the leaves this grid does not use), so each arrival's
+// own count tells it the call number, and no state has to be read before
+// arriving.  Lane 0 of wavefront 0 folds the workgroup max into its leaf's
+// maxbits (non-negative floats order like their bit patterns) and only after
+// that atomic has returned adds to the leaf count.  The arrival that completes
+// a leaf adds to the root count; the one that completes the root takes every
+// leaf's max with an atomic exchange against 0 (one lane per leaf; this also
+// clears them for the next call) and writes rel = (call + 1, max) into all
+// kLeaves leaf lines.  Everyone else polls its own leaf's rel.  The poll is
+// bounded: after kSpinLimit polls it records timed_out and goes on (the
+// result is then unspecified and the workspace must be zero-filled again, but
+// every wavefront finishes).
 
 constexpr int kLine = 256;               // bytes per barrier line
 constexpr int kLeafWgs = 16;             // workgroups per leaf
@@ -517,13 +519,13 @@ constexpr size_t kPartialOffset = static_cast<size_t>(kLine) * (1 + kLeaves);
 constexpr unsigned kSpinLimit = 1u << 22;
 
 struct RootLine {
-  unsigned count;
+  unsigned long long count;
   unsigned timed_out;
 };
 
 struct LeafLine {
-  unsigned count;
-  unsigned maxbits[2];
+  unsigned long long count;
+  unsigned maxbits;
   unsigned pad;
   unsigned long long rel;
 };
@@ -542,55 +544,57 @@ __device__ __forceinline__ void store_agent(T* p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Release word of this workgroup's leaf, read at kernel start by wavefront 0.
-__device__ __forceinline__ unsigned long long leaf_release_word(char* ws) {
-  return load_agent(&leaf_line(ws, blockIdx.x / kLeafWgs)->rel);
+template <typename T>
+__device__ __forceinline__ T add_agent(T* p, T v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Grid-wide max; called by the 64 lanes of wavefront 0 with the workgroup's
-// max (uniform) and the leaf's release word from kernel start.  Every lane
-// returns the tensor-wide max.
-__device__ float grid_max_wave0(float wg_max, char* __restrict__ ws, unsigned long long rel0) {
+// max (uniform).  Every lane returns the tensor-wide max.
+__device__ float grid_max_wave0(float wg_max, char* __restrict__ ws) {
   const int lane = threadIdx.x & 63;
   RootLine* root = reinterpret_cast<RootLine*>(ws);
   const unsigned l = blockIdx.x / kLeafWgs;
   const unsigned nleaves = (gridDim.x + kLeafWgs - 1) / kLeafWgs;
   const unsigned in_leaf = min(static_cast<unsigned>(kLeafWgs), gridDim.x - l * kLeafWgs);
   LeafLine* lf = leaf_line(ws, l);
-  const unsigned gen0 = static_cast<unsigned>(rel0 >> 32), slot = gen0 & 1;
+  unsigned long long call = 0;
   unsigned role = 0;   // 0: wait for the release; 2: complete the barrier
   if (lane == 0) {
-    const unsigned prev = __hip_atomic_fetch_max(&lf->maxbits[slot], __float_as_uint(wg_max),
+    const unsigned prev = __hip_atomic_fetch_max(&lf->maxbits, __float_as_uint(wg_max),
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // prev is a finite float pattern, never ~0u: the add cannot be issued
     // before the max has returned.
-    const unsigned inc = prev == ~0u ? 2u : 1u;
-    if (__hip_atomic_fetch_add(&lf->count, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
-        in_leaf) {
-      store_agent(&lf->count, 0u);
-      if (__hip_atomic_fetch_add(&root->count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 ==
-          nleaves) {
-        store_agent(&root->count, 0u);
-        role = 2;
-      }
+    unsigned long long inc = prev == ~0u ? 2 : 1;
+    if (blockIdx.x % kLeafWgs == 0) inc += kLeafWgs - in_leaf;
+    const unsigned long long a = add_agent(&lf->count, inc) + inc;
+    call = (a - 1) / kLeafWgs;
+    if (a % kLeafWgs == 0) {
+      const unsigned long long rinc = 1 + (l == 0 ? kLeaves - nleaves : 0);
+      if ((add_agent(&root->count, rinc) + rinc) % kLeaves == 0) role = 2;
     }
   }
   role = __builtin_amdgcn_readfirstlane(role);
+  call = (static_cast<unsigned long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(call >> 32))) << 32) |
+         __builtin_amdgcn_readfirstlane(static_cast<unsigned>(call));
+  const unsigned long long want = (call + 1) << 32;
   if (role == 2) {
-    unsigned mx = 0;
-    if (lane < static_cast<int>(nleaves)) mx = load_agent(&leaf_line(ws, lane)->maxbits[slot]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = max(mx, static_cast<unsigned>(__shfl_xor(static_cast<int>(mx), o)));
-    const unsigned long long rel = (static_cast<unsigned long long>(gen0 + 1) << 32) | mx;
     LeafLine* o = leaf_line(ws, lane);          // kLeaves == 64: one leaf per lane
-    store_agent(&o->maxbits[slot ^ 1], 0u);
-    store_agent(&o->rel, rel);
+    unsigned mx = 0;
+    if (lane < static_cast<int>(nleaves)) {
+      mx = __hip_atomic_exchange(&o->maxbits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      store_agent(&o->count, (call + 1) * kLeafWgs);   // unused this call: keep in step
+    }
+#pragma unroll
+    for (int k = 32; k > 0; k >>= 1) mx = max(mx, static_cast<unsigned>(__shfl_xor(static_cast<int>(mx), k)));
+    store_agent(&o->rel, want | mx);
     return __uint_as_float(mx);
   }
   unsigned long long r = 0;
   if (lane == 0) {
     unsigned spins = 0;
-    while (static_cast<unsigned>((r = load_agent(&lf->rel)) >> 32) == gen0) {
+    while (((r = load_agent(&lf->rel)) >> 32) != (want >> 32)) {
       if (++spins == kSpinLimit) {
         store_agent(&root->timed_out, 1u);
         break;
@@ -627,8 +631,9 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + (threadIdx.x >> 6);
   const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
-  unsigned long long rel0 = 0;
-  if (threadIdx.x < 64) rel0 = leaf_release_word(ws);
+  // No branch may separate these loads from their first use: the compiler
+  // would wait for every outstanding load at the join.  Tiles past the end
+  // load (and below store) the last tile again, with identical values.
   uint4 xr[TPW][NK];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
@@ -641,9 +646,10 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int64_t t = wid + i * nw;
-    const int rv = rows_valid(t < ntiles ? t : ntiles - 1, nblocks);
+    const int64_t tc = t < ntiles ? t : ntiles - 1;
+    const int rv = rows_valid(tc, nblocks);
     al[i] = ash_scale(column_sum_squares<B>(xr[i]), sqrt_eb);
-    if (t < ntiles) alpha[t * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
+    alpha[tc * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
     float m = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) {
@@ -656,7 +662,7 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
   }
   const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x < 64) {
-    const float A = grid_max_wave0(wg, ws, rel0);
+    const float A = grid_max_wave0(wg, ws);
     if (threadIdx.x == 0) amax_sh = A;
   }
   __syncthreads();

@@ -190,7 +190,7 @@ def test_fused_matches_two_pass_bitwise(taco):
         two = _compress_with(taco, x, block, False, ws)
         for a, b in zip(fused, two):
             assert torch.equal(a, b)
-        timed_out = int(ws[4:8].cpu().numpy().view(np.uint32)[0])
+        timed_out = int(ws[8:12].cpu().numpy().view(np.uint32)[0])
         assert timed_out == 0
 
 
