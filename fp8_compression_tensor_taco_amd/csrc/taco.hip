@@ -59,7 +59,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kThreadsC = 1024;         // compress workgroups: 16 wavefronts
 constexpr int kWavesC = kThreadsC / 64;
 constexpr float kQmax = 448.0f;         // largest E4M3FN magnitude
-constexpr int kMaxPartials = 4096;      // workgroups of the statistics pass
+constexpr int kMaxPartials = 1024;      // workgroups of the statistics pass (at most)
 
 constexpr int kQuadXor1 = 0xB1;         // DPP quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;         // DPP quad_perm [2,3,0,1]
@@ -80,6 +80,53 @@ struct Blk {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // ----------------------------------------------------------------- helpers
+
+// Streaming accesses.  Non-temporal stores of the outputs leave no dirty
+// lines in L2 for the end-of-kernel write-back (measured: compress 17.2 ->
+// 15.0 us, decompress 13.7 -> 12.1 us per call on [4096, 4096]; the
+// decompress-sum output measured no better, so it keeps ordinary stores).
+// x is read non-temporally by the fused kernel (14.9 -> 14.2 us), but not by
+// the two-pass kernels (the quantisation pass reads the statistics pass's
+// data again from the cache; non-temporal loads there measured slower).
+// Non-temporal code loads measured slower too (decompress 12.0 -> 15.8 us).
+#ifndef TACO_NT_Q_LOADS
+#define TACO_NT_Q_LOADS 0
+#endif
+#ifndef TACO_NT_CODE_STORES
+#define TACO_NT_CODE_STORES 1
+#endif
+#ifndef TACO_NT_OUT_STORES
+#define TACO_NT_OUT_STORES 1
+#endif
+#ifndef TACO_NT_SUM_STORES
+#define TACO_NT_SUM_STORES 0
+#endif
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ void store16(uint4* p, const uint4 v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(p));
+  else
+    *p = v;
+}
+
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const uint4* p) {
+  if constexpr (NT)
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+  else
+    return *p;
+}
+
+template <bool NT>
+__device__ __forceinline__ uint2 load8(const uint2* p) {
+  if constexpr (NT)
+    return __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p)));
+  else
+    return *p;
+}
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -213,25 +260,10 @@ __device__ __forceinline__ uint4 to_bf16x8(const float (&v)[8], float c) {
                     pack_bf16x2(v[4] * c, v[5] * c), pack_bf16x2(v[6] * c, v[7] * c));
 }
 
-// Per-wavefront tile walk: wavefront `wid` of `nwaves` owns tiles
-// wid, wid + nwaves, ...; `reverse` walks them from the last one back.
-struct Walk {
-  int64_t wid, nwaves, ntiles, count;
-  __device__ __forceinline__ Walk(int waves_per_wg, int64_t nblocks) {
-    wid = static_cast<int64_t>(blockIdx.x) * waves_per_wg + (threadIdx.x >> 6);
-    nwaves = static_cast<int64_t>(gridDim.x) * waves_per_wg;
-    ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
-    count = wid < ntiles ? (ntiles - wid + nwaves - 1) / nwaves : 0;
-  }
-  __device__ __forceinline__ int64_t tile(int64_t j, bool reverse) const {
-    return wid + (reverse ? count - 1 - j : j) * nwaves;
-  }
-};
-
 // Lane-linear transfer of a tile between global memory and its padded LDS
 // image: tile row r (block 16t + r) holds ROW bytes, stored at r * STRIDE.
 // Only rows of blocks that exist are transferred.
-template <int ROW, int STRIDE>
+template <int ROW, int STRIDE, bool NT>
 __device__ __forceinline__ void lds_store_tile_to_global(const char* lds, uint4* __restrict__ g,
                                                          int64_t tile, int rows_valid) {
   constexpr int kChunksPerRow = ROW / 16, kChunks = kTileBlocks * kChunksPerRow;
@@ -241,7 +273,7 @@ __device__ __forceinline__ void lds_store_tile_to_global(const char* lds, uint4*
 #pragma unroll
     for (int i = 0; i < kChunks / 64; ++i) {
       const int c = 64 * i + lane;
-      base[c] = *reinterpret_cast<const uint4*>(lds + (c / kChunksPerRow) * STRIDE + 16 * (c % kChunksPerRow));
+      store16<NT>(&base[c], *reinterpret_cast<const uint4*>(lds + (c / kChunksPerRow) * STRIDE + 16 * (c % kChunksPerRow)));
     }
     return;
   }
@@ -250,22 +282,13 @@ __device__ __forceinline__ void lds_store_tile_to_global(const char* lds, uint4*
     const int c = 64 * i + lane;
     const int r = c / kChunksPerRow, col = c % kChunksPerRow;
     if (c < kChunks && r < rows_valid)
-      base[c] = *reinterpret_cast<const uint4*>(lds + r * STRIDE + 16 * col);
+      store16<NT>(&base[c], *reinterpret_cast<const uint4*>(lds + r * STRIDE + 16 * col));
   }
 }
 
 __device__ __forceinline__ int rows_valid(int64_t tile, int64_t nblocks) {
   const int64_t r = nblocks - tile * kTileBlocks;
   return r >= kTileBlocks ? kTileBlocks : static_cast<int>(r);
-}
-
-// Max of the first n values of `partial`, computed by one wavefront (every lane
-// gets it); no workgroup barrier, so it overlaps with the wavefront's loads.
-__device__ __forceinline__ float wave_max_of(const float* __restrict__ partial, int n) {
-  const int lane = threadIdx.x & 63;
-  float m = 0.0f;
-  for (int i = lane; i < n; i += 64) m = fmaxf(m, partial[i]);
-  return wave_max(m);
 }
 
 // Lane geometry of the quad layout inside a 16-block tile.
@@ -360,7 +383,7 @@ __device__ __forceinline__ float column_sum_squares(const uint4 (&xr)[B / 32]) {
 // The B operand of one tile.  Loads are branch-free: lanes whose block lies
 // past the end of the tensor read the tile's last block instead, and their
 // results are never stored (or are duplicates of a valid column's).
-template <int B>
+template <int B, bool NT>
 __device__ __forceinline__ void load_tile_mfma(const uint4* __restrict__ x, int64_t t, int64_t nblocks,
                                                uint4 (&xr)[B / 32]) {
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
@@ -368,113 +391,120 @@ __device__ __forceinline__ void load_tile_mfma(const uint4* __restrict__ x, int6
   const uint4* tile = x + t * (kTileBlocks * Blk<B>::C16);
   const int row = n < rv ? n : rv - 1;
 #pragma unroll
-  for (int kt = 0; kt < B / 32; ++kt) xr[kt] = tile[row * Blk<B>::C16 + 4 * kt + g];
+  for (int kt = 0; kt < B / 32; ++kt) xr[kt] = load16<NT>(&tile[row * Blk<B>::C16 + 4 * kt + g]);
 }
 
-// Statistics of one tile: stores alpha of its blocks and returns this lane's
-// max of alpha_k * |y_raw| / sqrt(B) (0 for a column past the end).
+// Codes of rows 16 mt .. 16 mt + 15 of a tile's rotated blocks (MFMA C
+// layout): scale by c, convert, and place them in the wavefront's LDS tile.
 template <int B>
-__device__ __forceinline__ float stats_tile_mfma(const HadFrag& F, const uint4 (&xr)[B / 32], int64_t t,
-                                                 int64_t nblocks, float sqrt_eb, float* __restrict__ alpha) {
-  const int lane = threadIdx.x & 63, n = lane & 15;
-  const int rv = rows_valid(t, nblocks);
-  const int row = n < rv ? n : rv - 1;
-  const float a = ash_scale(column_sum_squares<B>(xr), sqrt_eb);
-  alpha[t * kTileBlocks + row] = a;           // duplicates write identical values
-  float m = 0.0f;
-#pragma unroll
-  for (int mt = 0; mt < B / 16; ++mt) {
-    const f32x4_t y = hadamard_mtile<B>(F, xr, mt);
-    m = fmaxf(fmaxf(m, fabsf(y[0])), fabsf(y[1]));
-    m = fmaxf(fmaxf(m, fabsf(y[2])), fabsf(y[3]));
-  }
-  return n < rv ? m * (a * Blk<B>::rsqrt_b) : 0.0f;
-}
-
-// Codes of one tile: quantised in the MFMA C layout into the wavefront's LDS
-// tile, then stored lane-linearly.
-template <int B>
-__device__ __forceinline__ void quant_tile_mfma(const HadFrag& F, const uint4 (&xr)[B / 32], int64_t t,
-                                                int64_t nblocks, float sqrt_eb, float s, char* lds,
-                                                uint4* __restrict__ q) {
-  constexpr int SROW = Blk<B>::kCodeRowMfma;
+__device__ __forceinline__ void codes_to_lds_mfma(const f32x4_t y, float c, int mt, char* lds) {
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  const float c = (ash_scale(column_sum_squares<B>(xr), sqrt_eb) * s) * Blk<B>::rsqrt_b;
-#pragma unroll
-  for (int mt = 0; mt < B / 16; ++mt) {
-    const f32x4_t y = hadamard_mtile<B>(F, xr, mt);
-    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * c, y[1] * c, 0, false);
-    wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * c, y[3] * c, wd, true);
-    *reinterpret_cast<int*>(lds + n * SROW + 16 * mt + 4 * g) = wd;
-  }
-  __builtin_amdgcn_wave_barrier();
-  lds_store_tile_to_global<B, SROW>(lds, q, t, rows_valid(t, nblocks));
-  __builtin_amdgcn_wave_barrier();
+  int wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * c, y[1] * c, 0, false);
+  wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * c, y[3] * c, wd, true);
+  *reinterpret_cast<int*>(lds + n * Blk<B>::kCodeRowMfma + 16 * mt + 4 * g) = wd;
 }
 
-// Software pipeline over a wavefront's tiles, two deep: the loads of tile j+2
-// are issued right after tile j is consumed.  The steady-state body is
-// straight-line code (no branches around loads), so the compiler waits only
-// for the tile about to be used; the last one to three tiles are handled
-// after the loop.
-#define TACO_PIPELINE_2(COUNT, LOAD, WORK)                                    \
-  do {                                                                        \
-    const int64_t cnt_ = (COUNT);                                             \
-    if (cnt_ > 0) {                                                           \
-      LOAD(xa_, 0);                                                           \
-      if (cnt_ > 1) LOAD(xb_, 1);                                             \
-      int64_t j_ = 0;                                                         \
-      for (; j_ + 3 < cnt_; j_ += 2) {                                        \
-        WORK(xa_, j_);                                                        \
-        LOAD(xa_, j_ + 2);                                                    \
-        WORK(xb_, j_ + 1);                                                    \
-        LOAD(xb_, j_ + 3);                                                    \
-      }                                                                       \
-      WORK(xa_, j_);                                                          \
-      if (j_ + 2 < cnt_) LOAD(xa_, j_ + 2);                                   \
-      if (j_ + 1 < cnt_) WORK(xb_, j_ + 1);                                   \
-      if (j_ + 2 < cnt_) WORK(xa_, j_ + 2);                                   \
-    }                                                                         \
-  } while (0)
-
-template <int B>
+// Two-pass compression, for tensors whose rotated blocks do not fit in the
+// resident wavefronts' registers (or when the single pass is switched off):
+// a statistics kernel (alpha and per-workgroup max) and a quantisation kernel
+// that folds the workgroup maxima into s, re-reads x and writes the codes.
+// Both give each wavefront U tiles per trip (wid, wid + W, ... for W
+// wavefronts in the grid), issue all of a trip's loads before using any, and
+// keep every branch away from loads in flight (the compiler waits for all
+// outstanding loads at a join).  Tiles past the end load, and write alpha
+// for, the last tile again (identical values).  The arithmetic per tile is
+// the fused kernel's, instruction for instruction, so the results are
+// bitwise identical.
+template <int B, int U>
 __global__ __launch_bounds__(kThreads) void compress_stats_mfma_kernel(
     const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb,
     float* __restrict__ alpha, float* __restrict__ partial) {
-  constexpr int NK = B / 32;
+  constexpr int NK = B / 32, NM = B / 16;
   __shared__ float red[kWaves];
   const HadFrag F = make_hadamard_fragments();
-  const Walk w(kWaves, nblocks);
-  uint4 xa_[NK], xb_[NK];
+  const int n = threadIdx.x & 15;
+  const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
   float amax = 0.0f;
-#define LOAD(buf, j) load_tile_mfma<B>(x, w.tile(j, false), nblocks, buf)
-#define WORK(buf, j) amax = fmaxf(amax, stats_tile_mfma<B>(F, buf, w.tile(j, false), nblocks, sqrt_eb, alpha))
-  TACO_PIPELINE_2(w.count, LOAD, WORK);
-#undef LOAD
-#undef WORK
+  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
+       t0 += nw * U) {
+    uint4 xr[U][NK];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = t0 + u * nw;
+      load_tile_mfma<B, false>(x, t < ntiles ? t : ntiles - 1, nblocks, xr[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = t0 + u * nw;
+      const int64_t tc = t < ntiles ? t : ntiles - 1;
+      const int rv = rows_valid(tc, nblocks);
+      const float al = ash_scale(column_sum_squares<B>(xr[u]), sqrt_eb);
+      alpha[tc * kTileBlocks + (n < rv ? n : rv - 1)] = al;
+      float m = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) {
+        const f32x4_t v = hadamard_mtile<B>(F, xr[u], mt);
+        m = fmaxf(fmaxf(m, fabsf(v[0])), fabsf(v[1]));
+        m = fmaxf(fmaxf(m, fabsf(v[2])), fabsf(v[3]));
+      }
+      if (t < ntiles && n < rv) amax = fmaxf(amax, m * (al * Blk<B>::rsqrt_b));
+    }
+  }
   const float wg = workgroup_max<kWaves>(amax, red);
   if (threadIdx.x == 0) partial[blockIdx.x] = wg;
 }
 
-template <int B>
+// Max of the n (<= kMaxPartials) workgroup maxima; every thread of the
+// workgroup takes part (kMaxPartials / kThreads loads each, issued together,
+// indices clamped so that no branch surrounds them) and gets the result.
+__device__ __forceinline__ float partials_max(const float* __restrict__ partial, int n, float* red) {
+  constexpr int kPer = kMaxPartials / kThreads;
+  float v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int i = static_cast<int>(threadIdx.x) + kThreads * k;
+    v[k] = partial[i < n ? i : n - 1];
+  }
+  float m = v[0];
+#pragma unroll
+  for (int k = 1; k < kPer; ++k) m = fmaxf(m, v[k]);
+  return workgroup_max<kWaves>(m, red);
+}
+
+template <int B, int U>
 __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
     const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb,
     const float* __restrict__ partial, int npartial, float* __restrict__ scale,
     uint4* __restrict__ q) {
-  constexpr int NK = B / 32, SROW = Blk<B>::kCodeRowMfma;
+  constexpr int NK = B / 32, NM = B / 16, SROW = Blk<B>::kCodeRowMfma;
+  __shared__ float red[kWaves];
   __shared__ __attribute__((aligned(16))) char lds_all[kWaves][kTileBlocks * SROW];
   char* lds = lds_all[threadIdx.x >> 6];
   const HadFrag F = make_hadamard_fragments();
-  const Walk w(kWaves, nblocks);
-  const float A = wave_max_of(partial, npartial);
+  const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  uint4 xr[U][NK];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t t = t0 + u * nw;
+    load_tile_mfma<B, false>(x, t < ntiles ? t : ntiles - 1, nblocks, xr[u]);
+  }
+  const float A = partials_max(partial, npartial, red);
   const float s = A > 0.0f ? kQmax / A : 1.0f;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int64_t t = t0 + u * nw;
+    if (t >= ntiles) break;
+    const float c = (ash_scale(column_sum_squares<B>(xr[u]), sqrt_eb) * s) * Blk<B>::rsqrt_b;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) codes_to_lds_mfma<B>(hadamard_mtile<B>(F, xr[u], mt), c, mt, lds);
+    __builtin_amdgcn_wave_barrier();
+    lds_store_tile_to_global<B, SROW, TACO_NT_CODE_STORES != 0>(lds, q, t, rows_valid(t, nblocks));
+    __builtin_amdgcn_wave_barrier();
+  }
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
-  uint4 xa_[NK], xb_[NK];
-#define LOAD(buf, j) load_tile_mfma<B>(x, w.tile(j, false), nblocks, buf)
-#define WORK(buf, j) quant_tile_mfma<B>(F, buf, w.tile(j, false), nblocks, sqrt_eb, s, lds, q)
-  TACO_PIPELINE_2(w.count, LOAD, WORK);
-#undef LOAD
-#undef WORK
 }
 
 // ============================================================== fused compress
@@ -606,16 +636,6 @@ __device__ float grid_max_wave0(float wg_max, char* __restrict__ ws) {
 }
 static_assert(kLeaves == 64, "grid_max_wave0 releases one leaf per lane");
 
-// Codes of rows 16 mt .. 16 mt + 15 of a tile's rotated blocks (MFMA C
-// layout): scale by c, convert, and place them in the wavefront's LDS tile.
-template <int B>
-__device__ __forceinline__ void codes_to_lds_mfma(const f32x4_t y, float c, int mt, char* lds) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  int wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[0] * c, y[1] * c, 0, false);
-  wd = __builtin_amdgcn_cvt_pk_fp8_f32(y[2] * c, y[3] * c, wd, true);
-  *reinterpret_cast<int*>(lds + n * Blk<B>::kCodeRowMfma + 16 * mt + 4 * g) = wd;
-}
-
 // Wavefront w of W owns tiles w, w + W, ..., w + (TPW-1) W (those < ntiles).
 template <int B, int TPW, bool HOLD_Y, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
@@ -638,7 +658,7 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int64_t t = wid + i * nw;
-    load_tile_mfma<B>(x, t < ntiles ? t : ntiles - 1, nblocks, xr[i]);
+    load_tile_mfma<B, true>(x, t < ntiles ? t : ntiles - 1, nblocks, xr[i]);
   }
   f32x4_t y[HOLD_Y ? TPW : 1][NM];
   float al[TPW];
@@ -682,7 +702,7 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
       for (int mt = 0; mt < NM; ++mt) codes_to_lds_mfma<B>(hadamard_mtile<B>(F, xr[i], mt), c, mt, lds);
     }
     __builtin_amdgcn_wave_barrier();
-    lds_store_tile_to_global<B, SROW>(lds, q, t, rows_valid(t, nblocks));
+    lds_store_tile_to_global<B, SROW, TACO_NT_CODE_STORES != 0>(lds, q, t, rows_valid(t, nblocks));
     __builtin_amdgcn_wave_barrier();
   }
 }
@@ -721,7 +741,8 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
       const int64_t k = (t0 + u * W) * kTileBlocks + qd.blk;
       const bool ok = t0 + u * W < ntiles && k < nblocks;
 #pragma unroll
-      for (int a = 0; a < NA; ++a) raw[u][a] = ok ? q[k * C16 + 4 * a + qd.ql] : make_uint2(0, 0);
+      for (int a = 0; a < NA; ++a)
+        raw[u][a] = ok ? load8<TACO_NT_Q_LOADS != 0>(&q[k * C16 + 4 * a + qd.ql]) : make_uint2(0, 0);
       al[u] = ok ? alpha[k] : 1.0f;
     }
 #pragma unroll
@@ -736,7 +757,7 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         const uint4 o = to_bf16x8(v[a], r);
-        if (ok) out[k * C16 + 4 * a + qd.ql] = o;
+        if (ok) store16<TACO_NT_OUT_STORES != 0>(&out[k * C16 + 4 * a + qd.ql], o);
       }
     }
   }
@@ -776,7 +797,8 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
       for (int p = 0; p < P; ++p) {
         const uint2* qp = reinterpret_cast<const uint2*>(parts.q[p]);
 #pragma unroll
-        for (int a = 0; a < NA; ++a) raw[u][p][a] = ok ? qp[k * C16 + 4 * a + qd.ql] : make_uint2(0, 0);
+        for (int a = 0; a < NA; ++a)
+          raw[u][p][a] = ok ? load8<TACO_NT_Q_LOADS != 0>(&qp[k * C16 + 4 * a + qd.ql]) : make_uint2(0, 0);
         wt[u][p] = ok ? parts.alpha[p][k] : 1.0f;
       }
     }
@@ -805,18 +827,13 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         const uint4 o = to_bf16x8(acc[a], r);
-        if (ok) out[k * C16 + 4 * a + qd.ql] = o;
+        if (ok) store16<TACO_NT_SUM_STORES != 0>(&out[k * C16 + 4 * a + qd.ql], o);
       }
     }
   }
 }
 
 // ----------------------------------------------------------------- host side
-
-// Persistent kernels aim for at least this many tiles per wavefront (so the
-// software pipeline has something to overlap) but never fewer wavefronts than
-// min(tiles, 4 per CU).
-constexpr int64_t kTilesPerWave = 4;
 
 int device_cu_count() {
   int dev = 0;
@@ -868,19 +885,6 @@ taco_status_t launched() { return hipGetLastError() == hipSuccess ? TACO_OK : TA
 
 int g_engine = TACO_ENGINE_AUTO;   // rotation engine of taco_compress (process-wide)
 
-// Workgroups of a persistent kernel with `waves` wavefronts per workgroup.
-int persistent_grid(int64_t nblocks, int waves, int resident_wgs) {
-  const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
-  const int cus = device_cu_count() > 0 ? device_cu_count() : 256;
-  int64_t want = (tiles + kTilesPerWave - 1) / kTilesPerWave;          // wavefronts
-  const int64_t floor_waves = std::min<int64_t>(tiles, 4 * cus);
-  if (want < floor_waves) want = floor_waves;
-  int64_t g = (want + waves - 1) / waves;
-  if (g > resident_wgs) g = resident_wgs;
-  if (g < 1) g = 1;
-  return static_cast<int>(g);
-}
-
 // Launches the fused compress with TPW tiles per wavefront if every one of its
 // wavefronts can be resident at once (and the barrier has leaves for them).
 template <int B, int TPW, bool HOLD_Y, int WAVES>
@@ -922,13 +926,16 @@ void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, f
   float* partial = reinterpret_cast<float*>(ws + kPartialOffset);
   // Single fused pass when the tensor fits in the resident wavefronts' VGPRs.
   if (g_single_pass && launch_fused<B>(xv, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
-  static const int cap = std::min(resident_grid(compress_stats_mfma_kernel<B>, kThreads),
-                                  resident_grid(compress_quant_mfma_kernel<B>, kThreads));
-  const int g = persistent_grid(nblocks, kWaves, std::min(cap, kMaxPartials));
-  hipLaunchKernelGGL((compress_stats_mfma_kernel<B>), dim3(g), dim3(kThreads), 0, stream,
+  constexpr int U = 2;
+  const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t per_wg = static_cast<int64_t>(kWaves) * U;
+  const int64_t want = (tiles + per_wg - 1) / per_wg;
+  const int gs = static_cast<int>(std::min<int64_t>(want, kMaxPartials));
+  const int gq = static_cast<int>(std::min<int64_t>(want, INT32_MAX));
+  hipLaunchKernelGGL((compress_stats_mfma_kernel<B, U>), dim3(gs), dim3(kThreads), 0, stream,
                      xv, nblocks, sqrt_eb, alpha, partial);
-  hipLaunchKernelGGL((compress_quant_mfma_kernel<B>), dim3(g), dim3(kThreads), 0, stream,
-                     xv, nblocks, sqrt_eb, partial, g, scale, qv);
+  hipLaunchKernelGGL((compress_quant_mfma_kernel<B, U>), dim3(gq), dim3(kThreads), 0, stream,
+                     xv, nblocks, sqrt_eb, partial, gs, scale, qv);
 }
 
 template <int B>
