@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     set_single_pass,
     decompress,
     decompress_sum,
+    decompress_sum_compress,
     library_path,
     load,
     num_scales,
@@ -22,7 +23,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "TACO_MAX_PARTS", "TacoError", "compress", "decompress", "decompress_sum", "get_rotation_engine",
+    "TACO_MAX_PARTS", "TacoError", "compress", "decompress", "decompress_sum", "decompress_sum_compress", "get_rotation_engine",
     "get_single_pass", "library_path", "load", "num_scales", "set_rotation_engine", "set_single_pass",
     "version", "workspace_bytes",
 ]

@@ -19,7 +19,7 @@ TACO_MAX_PARTS = 8
 _STATUS = {
     0: "TACO_OK", 1: "TACO_ERR_NULL", 2: "TACO_ERR_ALIGN", 3: "TACO_ERR_SHAPE",
     4: "TACO_ERR_UNSUPPORTED_BLOCK", 5: "TACO_ERR_BAD_ENERGY", 6: "TACO_ERR_WORKSPACE",
-    7: "TACO_ERR_BAD_NPARTS", 8: "TACO_ERR_HIP", 9: "TACO_ERR_BAD_ENGINE",
+    7: "TACO_ERR_BAD_NPARTS", 8: "TACO_ERR_HIP", 9: "TACO_ERR_BAD_ENGINE", 10: "TACO_ERR_ALIAS",
 }
 ENGINES = {"auto": 0, "valu": 1, "mfma": 2}
 
@@ -35,7 +35,7 @@ class TacoError(RuntimeError):
 
 _lib = None
 _lock = threading.Lock()
-_workspaces: dict[int, torch.Tensor] = {}
+_workspaces: dict[tuple[int, str], torch.Tensor] = {}
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -78,6 +78,13 @@ def load() -> ctypes.CDLL:
                                       _vp, ctypes.c_size_t, _vp]
         lib.taco_decompress.restype = ctypes.c_int
         lib.taco_decompress.argtypes = [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+        lib.taco_decompress_sum_compress_workspace_bytes.restype = ctypes.c_size_t
+        lib.taco_decompress_sum_compress_workspace_bytes.argtypes = [_i64, _i64, _i32]
+        lib.taco_decompress_sum_compress.restype = ctypes.c_int
+        lib.taco_decompress_sum_compress.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                                     ctypes.POINTER(_vp), _i32, _i64, _i64, _i32,
+                                                     ctypes.c_float, _vp, _vp, _vp, _vp,
+                                                     ctypes.c_size_t, _vp]
         lib.taco_decompress_sum.restype = ctypes.c_int
         lib.taco_decompress_sum.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                             ctypes.POINTER(_vp), _i32, _i64, _i64, _i32, _vp, _vp]
@@ -158,12 +165,14 @@ def workspace_bytes(tokens: int, hidden: int, block: int) -> int:
     return int(load().taco_compress_workspace_bytes(tokens, hidden, block))
 
 
-def _workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+def _workspace(device: torch.device, nbytes: int, kind: str = "compress") -> torch.Tensor:
+    """A zero-filled workspace per device and kind, grown when too small (a new
+    one starts zeroed, as the library requires)."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _workspaces.get(idx)
+    ws = _workspaces.get((idx, kind))
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
-        _workspaces[idx] = ws
+        _workspaces[(idx, kind)] = ws
     return ws
 
 
@@ -227,6 +236,61 @@ def decompress(q: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, block:
     _check(lib.taco_decompress(_ptr(q.contiguous()), _ptr(alpha.contiguous()), _ptr(scale), T, H,
                                block, _ptr(out), _stream(dev, stream)))
     return out
+
+
+def _check_parts(lib, parts):
+    parts = [(q.contiguous(), a.contiguous(), s) for q, a, s in parts]
+    if not 1 <= len(parts) <= TACO_MAX_PARTS:
+        _check(7)
+    dev = _require_gpu(*[t for p in parts for t in p])
+    return parts, dev
+
+
+def decompress_sum_compress(parts, block: int, target_energy: float = 1.0, *,
+                            q: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
+                            scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                            stream=None):
+    """compress(decompress_sum(parts)) in one call: returns (q, alpha, scale) of
+    the bf16 sum of the parts' reconstructions."""
+    lib = load()
+    parts, dev = _check_parts(lib, parts)
+    T, H = parts[0][0].shape
+    for pq, pa, ps in parts:
+        if pq.shape != (T, H) or pq.dtype != torch.uint8:
+            raise ValueError("every part's q must be uint8 with the same shape")
+        if pa.dtype != torch.float32 or ps.dtype != torch.float32:
+            raise ValueError("alpha and scale must be float32")
+        if pa.numel() != max(lib.taco_num_scales(T, H, block), 0):
+            raise ValueError("alpha has the wrong number of elements for this shape and block")
+        if ps.numel() < 1:
+            raise ValueError("scale must hold one float32")
+    n = lib.taco_num_scales(T, H, block)
+    if n < 0:
+        _check(4 if block not in (64, 128, 256) else 3)
+    if q is None:
+        q = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    if alpha is None:
+        alpha = torch.empty((T, H // block), dtype=torch.float32, device=dev)
+    if scale is None:
+        scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    need = lib.taco_decompress_sum_compress_workspace_bytes(T, H, block)
+    if workspace is None:
+        workspace = _workspace(dev, need, "decompress_sum_compress")
+    _require_gpu(parts[0][0], q, alpha, scale, workspace)
+    _require_buffer(q, "q", torch.uint8, T * H, (T, H))
+    _require_buffer(alpha, "alpha", torch.float32, n)
+    _require_buffer(scale, "scale", torch.float32, 1)
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    P = len(parts)
+    qa = (_vp * P)(*[p[0].data_ptr() for p in parts])
+    aa = (_vp * P)(*[p[1].data_ptr() for p in parts])
+    sa = (_vp * P)(*[p[2].data_ptr() for p in parts])
+    _check(lib.taco_decompress_sum_compress(qa, aa, sa, P, T, H, block, float(target_energy),
+                                            _ptr(q), _ptr(alpha), _ptr(scale), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(),
+                                            _stream(dev, stream)))
+    return q, alpha, scale
 
 
 def decompress_sum(parts, block: int, *, out: torch.Tensor | None = None,

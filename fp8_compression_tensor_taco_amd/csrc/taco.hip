@@ -59,6 +59,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kThreadsC = 1024;         // compress workgroups: 16 wavefronts
 constexpr int kWavesC = kThreadsC / 64;
 constexpr float kQmax = 448.0f;         // largest E4M3FN magnitude
+constexpr float kMinEnergy = 0x1p-40f;  // accepted target energies
+constexpr float kMaxEnergy = 0x1p40f;
 constexpr int kMaxPartials = 1024;      // workgroups of the statistics pass (at most)
 
 constexpr int kQuadXor1 = 0xB1;         // DPP quad_perm [1,0,3,2]
@@ -369,15 +371,18 @@ __device__ __forceinline__ f32x4_t hadamard_mtile(const HadFrag& F, const uint4 
 // gfx950 row swaps: permlane32_swap pairs lane l with l^32 and permlane16_swap
 // pairs l with l^16.  Each step adds the same two operands in the same order
 // in both lanes of a pair, so every lane of the column gets the same sum.
-template <int B>
-__device__ __forceinline__ float column_sum_squares(const uint4 (&xr)[B / 32]) {
-  float ss = sum_squares_bf16<B / 32>(xr);
+__device__ __forceinline__ float column_sum_rows(float ss) {
   const unsigned u = __float_as_uint(ss);
   const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
   ss = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
   const unsigned v = __float_as_uint(ss);
   const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
   return __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+}
+
+template <int B>
+__device__ __forceinline__ float column_sum_squares(const uint4 (&xr)[B / 32]) {
+  return column_sum_rows(sum_squares_bf16<B / 32>(xr));
 }
 
 // The B operand of one tile.  Loads are branch-free: lanes whose block lies
@@ -769,6 +774,25 @@ struct Parts {
   const float* scale[TACO_MAX_PARTS];
 };
 
+// acc + d * w with the product rounded before the add (no fused
+// multiply-add), so that a part and its exact negation cancel to zero, as the
+// sum of their reconstructions does in exact arithmetic.
+__device__ __forceinline__ float add_product(float acc, float d, float w) {
+#pragma clang fp contract(off)
+  return acc + d * w;
+}
+
+// arr[i] for a wave-uniform runtime i, by a chain of selects: indexing the
+// kernel-argument array directly with a runtime index makes the compiler copy
+// it to scratch memory.
+template <typename T>
+__device__ __forceinline__ T pick(const T (&arr)[TACO_MAX_PARTS], int i) {
+  T r = arr[0];
+#pragma unroll
+  for (int k = 1; k < TACO_MAX_PARTS; ++k) r = i == k ? arr[k] : r;
+  return r;
+}
+
 // Decompress-and-sum.  The rotation is linear, so the parts are combined
 // before it: acc = sum_p decode(q_p) / (alpha_{p,k} s_p), then one rotation
 // and the 1/sqrt(B) factor.  This is the same sum as decompressing each part
@@ -819,7 +843,7 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
           float d[8];
           from_fp8x8(raw[u][p][a], d);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[a][j] = fmaf(d[j], wp, acc[a][j]);
+          for (int j = 0; j < 8; ++j) acc[a][j] = add_product(acc[a][j], d[j], wp);
         }
       }
       rotate_f32<NA>(acc, qd);
@@ -830,6 +854,146 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
         if (ok) store16<TACO_NT_SUM_STORES != 0>(&out[k * C16 + 4 * a + qd.ql], o);
       }
     }
+  }
+}
+
+// ============================================================== decompress-sum-compress
+//
+// The reduce-scatter local step with its result compressed again for the
+// all-gather leg [TACO pt-summary, 2.B.3]: compress(decompress_sum(parts)).
+// Fused when the reduced tensor's rotated blocks fit in the resident
+// wavefronts' VGPRs: each wavefront sums its tiles' parts in the Hadamard
+// domain and rounds to bf16 exactly as decompress_sum_kernel does (quad
+// layout), re-lays the bf16 tile out through LDS into the MFMA operand
+// layout, and continues as compress_fused_kernel (alpha, rotation on the
+// matrix cores, grid-wide max, codes).  The bf16 sum never reaches HBM, and
+// the result is bitwise equal to decompress_sum followed by compress.  The
+// part count is a runtime loop; the next part's codes are loaded before the
+// current part is accumulated.
+template <int B, int TPW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
+    Parts parts, int nparts, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
+    float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q) {
+  constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16, NK = B / 32, NM = B / 16;
+  constexpr int XROW = 2 * B + 16, SROW = Blk<B>::kCodeRowMfma;
+  constexpr int kLdsWave = kTileBlocks * (XROW > SROW ? XROW : SROW);
+  __shared__ float red[WAVES];
+  __shared__ float amax_sh;
+  __shared__ __attribute__((aligned(16))) char lds_all[WAVES][kLdsWave];
+  char* lds = lds_all[threadIdx.x >> 6];
+  const Quad qd;
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + (threadIdx.x >> 6);
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
+  f32x4_t y[TPW][NM];
+  float al[TPW];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    const int64_t tc = t < ntiles ? t : ntiles - 1;
+    const int rv = rows_valid(tc, nblocks);
+    // this lane's block in the quad layout (rows past the end read the last block)
+    const int64_t kq = tc * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1);
+    float acc[NA][8];
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[a][j] = 0.0f;
+    uint2 cur[NA], nxt[NA];
+    float wcur, wnxt, scur, snxt;
+    {
+      const uint2* q0 = reinterpret_cast<const uint2*>(parts.q[0]);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) cur[a] = q0[kq * C16 + 4 * a + qd.ql];
+      wcur = parts.alpha[0][kq];
+      scur = *parts.scale[0];
+    }
+    for (int p = 0; p < nparts; ++p) {
+      const int pn = p + 1 < nparts ? p + 1 : p;        // the last trip reloads itself
+      const uint2* qn = reinterpret_cast<const uint2*>(pick(parts.q, pn));
+#pragma unroll
+      for (int a = 0; a < NA; ++a) nxt[a] = qn[kq * C16 + 4 * a + qd.ql];
+      wnxt = pick(parts.alpha, pn)[kq];
+      snxt = *pick(parts.scale, pn);
+      const float wp = 1.0f / (wcur * scur);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        float d[8];
+        from_fp8x8(cur[a], d);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[a][j] = add_product(acc[a][j], d[j], wp);
+      }
+#pragma unroll
+      for (int a = 0; a < NA; ++a) cur[a] = nxt[a];
+      wcur = wnxt;
+      scur = snxt;
+    }
+    rotate_f32<NA>(acc, qd);
+    const float r = Blk<B>::rsqrt_b * qd.debt;
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+      *reinterpret_cast<uint4*>(lds + qd.blk * XROW + 64 * a + 16 * qd.ql) = to_bf16x8(acc[a], r);
+    __builtin_amdgcn_wave_barrier();
+    // The MFMA operand is read from LDS one K-step at a time (few live
+    // registers); every sum is accumulated in the same order as
+    // column_sum_squares and hadamard_mtile, so the values are identical.
+    const HadFrag F = make_hadamard_fragments();
+    constexpr int kChains = NK >= 4 ? 4 : 2;
+    float ssq[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) ssq[c] = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) y[i][mt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kt = 0; kt < NK; ++kt) {
+      const uint4 xk = *reinterpret_cast<const uint4*>(lds + n * XROW + 64 * kt + 16 * g);
+      float& sc = ssq[kt % kChains];
+      sc = dot2_bf16(xk.x, xk.x, sc);
+      sc = dot2_bf16(xk.y, xk.y, sc);
+      sc = dot2_bf16(xk.z, xk.z, sc);
+      sc = dot2_bf16(xk.w, xk.w, sc);
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) {
+        const bool neg = __builtin_popcount((mt >> 1) & kt) & 1;
+        const bf16x8_t a = neg ? F.neg[mt & 1] : F.pos[mt & 1];
+        y[i][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, xk), y[i][mt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    float ss = ssq[0];
+#pragma unroll
+    for (int c = 1; c < kChains; ++c) ss += ssq[c];
+    al[i] = ash_scale(column_sum_rows(ss), sqrt_eb);
+    alpha[tc * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
+    float m = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) {
+      m = fmaxf(fmaxf(m, fabsf(y[i][mt][0])), fabsf(y[i][mt][1]));
+      m = fmaxf(fmaxf(m, fabsf(y[i][mt][2])), fabsf(y[i][mt][3]));
+    }
+    if (t < ntiles && n < rv) amax = fmaxf(amax, m * (al[i] * Blk<B>::rsqrt_b));
+  }
+  const float wg = workgroup_max<WAVES>(amax, red);
+  if (threadIdx.x < 64) {
+    const float A = grid_max_wave0(wg, ws);
+    if (threadIdx.x == 0) amax_sh = A;
+  }
+  __syncthreads();
+  const float A = amax_sh;
+  const float s = A > 0.0f ? kQmax / A : 1.0f;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    if (t >= ntiles) continue;
+    const float c = (al[i] * s) * Blk<B>::rsqrt_b;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) codes_to_lds_mfma<B>(y[i][mt], c, mt, lds);
+    __builtin_amdgcn_wave_barrier();
+    lds_store_tile_to_global<B, SROW, TACO_NT_CODE_STORES != 0>(lds, q, t, rows_valid(t, nblocks));
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -967,6 +1131,52 @@ void launch_decompress_sum(const Parts& parts, int nparts, int64_t nblocks, void
   }
 }
 
+// Bytes of the compress workspace proper (barrier lines and partial maxima),
+// rounded up so that the decompress-sum-compress intermediate after it is
+// 256-byte aligned.
+constexpr size_t kCompressWorkspace = (kPartialOffset + kMaxPartials * sizeof(float) + 255) / 256 * 256;
+
+template <int B, int TPW, int WAVES>
+bool try_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblocks, float sqrt_eb,
+                                 float* alpha, float* scale, char* ws, uint4* q, hipStream_t stream) {
+  static const int cap = std::min(resident_grid(decompress_sum_compress_kernel<B, TPW, WAVES>, 64 * WAVES),
+                                  kLeaves * kLeafWgs);
+  const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
+  if (g > cap) return false;
+  hipLaunchKernelGGL((decompress_sum_compress_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
+                     stream, parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, q);
+  return true;
+}
+
+// Fused when the reduced tensor fits on chip (fewest tiles per wavefront
+// first); otherwise the bf16 sum goes through the workspace and is compressed
+// as any other tensor.
+template <int B>
+void launch_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblocks, float energy,
+                                    uint8_t* q, float* alpha, float* scale, void* workspace,
+                                    hipStream_t stream) {
+  const float sqrt_eb = static_cast<float>(sqrt(static_cast<double>(energy) * B));
+  char* ws = static_cast<char*>(workspace);
+  uint4* qv = reinterpret_cast<uint4*>(q);
+  // 16 wavefronts per CU (128 VGPRs each) up to B = 128; at B = 256 the
+  // rotation of the sum needs more registers, so 8 wavefronts (256 VGPRs),
+  // two tiles each.
+  if (g_single_pass) {
+    if constexpr (B <= 128) {
+      if (try_decompress_sum_compress<B, 1, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
+      if (try_decompress_sum_compress<B, 2, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
+    } else {
+      if (try_decompress_sum_compress<B, 2, kWavesC / 2>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
+    }
+    if constexpr (B == 64)
+      if (try_decompress_sum_compress<B, 4, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
+  }
+  void* sum = ws + kCompressWorkspace;
+  launch_decompress_sum<B>(parts, nparts, nblocks, sum, stream);
+  launch_compress<B>(sum, nblocks, energy, q, alpha, scale, workspace, stream);
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------- C ABI
@@ -985,6 +1195,7 @@ const char* taco_status_string(taco_status_t status) {
     case TACO_ERR_BAD_NPARTS: return "TACO_ERR_BAD_NPARTS: nparts must be in [1, 8]";
     case TACO_ERR_HIP: return "TACO_ERR_HIP: a HIP call or kernel launch failed";
     case TACO_ERR_BAD_ENGINE: return "TACO_ERR_BAD_ENGINE: unknown rotation engine";
+    case TACO_ERR_ALIAS: return "TACO_ERR_ALIAS: an output buffer is also an input";
   }
   return "TACO_ERR_UNKNOWN";
 }
@@ -1026,7 +1237,7 @@ taco_status_t taco_compress(const void* x_bf16, int64_t tokens, int64_t hidden, 
   if (!aligned(x_bf16, 16) || !aligned(q_fp8, 16) || !aligned(alpha, 4) || !aligned(scale, 4) ||
       !aligned(workspace, 256))
     return TACO_ERR_ALIGN;
-  if (!(target_energy >= 0x1p-40f && target_energy <= 0x1p40f)) return TACO_ERR_BAD_ENERGY;
+  if (!(target_energy >= kMinEnergy && target_energy <= kMaxEnergy)) return TACO_ERR_BAD_ENERGY;
   if (workspace_bytes < taco_compress_workspace_bytes(tokens, hidden, block)) return TACO_ERR_WORKSPACE;
   if (device_cu_count() <= 0) return TACO_ERR_HIP;
   const int64_t nblocks = tokens * (hidden / block);
@@ -1087,3 +1298,43 @@ taco_status_t taco_decompress_sum(const uint8_t* const* q_fp8, const float* cons
 }
 
 }  // extern "C"
+
+size_t taco_decompress_sum_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block) {
+  if (check_shape(tokens, hidden, block) != TACO_OK) return 0;
+  return kCompressWorkspace + static_cast<size_t>(tokens) * static_cast<size_t>(hidden) * 2;
+}
+
+taco_status_t taco_decompress_sum_compress(const uint8_t* const* q_fp8, const float* const* alpha,
+                                           const float* const* scale, int32_t nparts, int64_t tokens,
+                                           int64_t hidden, int32_t block, float target_energy,
+                                           uint8_t* q_out, float* alpha_out, float* scale_out,
+                                           void* workspace, size_t workspace_bytes,
+                                           taco_stream_t stream) {
+  if (!q_fp8 || !alpha || !scale || !q_out || !alpha_out || !scale_out || !workspace) return TACO_ERR_NULL;
+  if (nparts < 1 || nparts > TACO_MAX_PARTS) return TACO_ERR_BAD_NPARTS;
+  const taco_status_t st = check_shape(tokens, hidden, block);
+  if (st != TACO_OK) return st;
+  if (!(target_energy >= kMinEnergy && target_energy <= kMaxEnergy)) return TACO_ERR_BAD_ENERGY;
+  Parts parts{};
+  for (int p = 0; p < nparts; ++p) {
+    if (!q_fp8[p] || !alpha[p] || !scale[p]) return TACO_ERR_NULL;
+    if (!aligned(q_fp8[p], 16) || !aligned(alpha[p], 4) || !aligned(scale[p], 4)) return TACO_ERR_ALIGN;
+    if (q_fp8[p] == q_out || alpha[p] == alpha_out || scale[p] == scale_out) return TACO_ERR_ALIAS;
+    parts.q[p] = reinterpret_cast<const uint4*>(q_fp8[p]);
+    parts.alpha[p] = alpha[p];
+    parts.scale[p] = scale[p];
+  }
+  if (!aligned(q_out, 16) || !aligned(alpha_out, 4) || !aligned(scale_out, 4) || !aligned(workspace, 256))
+    return TACO_ERR_ALIGN;
+  if (workspace_bytes < taco_decompress_sum_compress_workspace_bytes(tokens, hidden, block))
+    return TACO_ERR_WORKSPACE;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  const int64_t nblocks = tokens * (hidden / block);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (block) {
+    case 64: launch_decompress_sum_compress<64>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s); break;
+    case 128: launch_decompress_sum_compress<128>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s); break;
+    default: launch_decompress_sum_compress<256>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s); break;
+  }
+  return launched();
+}

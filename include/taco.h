@@ -62,7 +62,8 @@ typedef enum {
   TACO_ERR_WORKSPACE = 6,         /* workspace smaller than required               */
   TACO_ERR_BAD_NPARTS = 7,        /* nparts outside [1, TACO_MAX_PARTS]            */
   TACO_ERR_HIP = 8,               /* a HIP runtime call or kernel launch failed    */
-  TACO_ERR_BAD_ENGINE = 9         /* unknown value passed to taco_set_rotation_engine */
+  TACO_ERR_BAD_ENGINE = 9,        /* unknown value passed to taco_set_rotation_engine */
+  TACO_ERR_ALIAS = 10             /* an output buffer is also one of the inputs      */
 } taco_status_t;
 
 /* How taco_compress evaluates the Hadamard rotation.  Both give the same
@@ -154,6 +155,40 @@ taco_status_t taco_decompress_sum(const uint8_t* const* q_fp8, const float* cons
                                   const float* const* scale, int32_t nparts,
                                   int64_t tokens, int64_t hidden, int32_t block,
                                   void* out_bf16, taco_stream_t stream);
+
+/* Bytes of device workspace taco_decompress_sum_compress needs: the compress
+ * workspace (barrier state and partial maxima, zero-filled once, as for
+ * taco_compress) followed by room for the bf16 sum, 2 * tokens * hidden bytes,
+ * which the call uses when the reduced tensor does not fit on chip.  0 for an
+ * invalid shape. */
+size_t taco_decompress_sum_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block);
+
+/*
+ * Decompress-sum-compress: the local step of the two-shot all-reduce with its
+ * result compressed again for the all-gather leg [TACO pt-summary, section
+ * 2.B.3: the compression kernels around the reduce-scatter and all-gather].
+ *   Result = taco_compress(taco_decompress_sum(parts)): the bf16 sum of the
+ *   parts' reconstructions (as taco_decompress_sum computes it) compressed
+ *   with its own per-block alpha and per-tensor scale, bitwise equal to the
+ *   two calls in sequence.  When the tensor fits on chip and single-pass mode
+ *   is on (taco_set_single_pass) it is one kernel and the bf16 sum never
+ *   reaches device memory; otherwise the sum goes through the workspace.
+ *   q_fp8, alpha, scale   HOST arrays of `nparts` DEVICE pointers (1 ..
+ *                         TACO_MAX_PARTS), as taco_decompress_sum
+ *   target_energy         as taco_compress
+ *   q_out, alpha_out, scale_out  out, as taco_compress; none may be one of
+ *                         the inputs (TACO_ERR_ALIAS)
+ *   workspace             at least taco_decompress_sum_compress_workspace_bytes(),
+ *                         256-byte aligned, zero-filled once; same ordering and
+ *                         residency rules as the taco_compress workspace
+ */
+taco_status_t taco_decompress_sum_compress(const uint8_t* const* q_fp8, const float* const* alpha,
+                                           const float* const* scale, int32_t nparts,
+                                           int64_t tokens, int64_t hidden, int32_t block,
+                                           float target_energy, uint8_t* q_out,
+                                           float* alpha_out, float* scale_out,
+                                           void* workspace, size_t workspace_bytes,
+                                           taco_stream_t stream);
 
 #ifdef __cplusplus
 }

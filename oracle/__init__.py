@@ -12,6 +12,7 @@ from .taco_oracle import (  # noqa: F401
     decompress,
     decompress_f64,
     decompress_sum,
+    decompress_sum_compress,
     ds_scale,
     e4m3_decode,
     e4m3_decode_code,

@@ -255,3 +255,16 @@ def decompress_sum(parts, block: int) -> np.ndarray:
         r = decompress_f64(q, alpha, s, block)
         acc = r if acc is None else acc + r
     return f64_to_bf16_bits(acc)
+
+
+def decompress_sum_compress(parts, block: int, target_energy: float = 1.0):
+    """The reduce-scatter local step of the two-shot all-reduce with its output
+    compressed again for the all-gather leg [TACO pt-summary, 2.B.3: compressed
+    two-shot all-reduce with the codec kernels around the exchange].
+
+    Reading: the reduced shard is what decompress_sum produces (the parts'
+    reconstructions summed and rounded once to bf16, the precision an
+    uncompressed all-reduce would carry), and it is compressed exactly as any
+    other bf16 tensor (its own alpha and per-tensor s).  So this is the
+    composition of the two steps, and it is pinned by their pins."""
+    return compress(decompress_sum(parts, block), block, target_energy)

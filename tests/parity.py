@@ -118,8 +118,9 @@ def decompress_error_bound(q, alpha, s, block):
 
 
 def decompress_sum_error_bound(parts, block):
-    """As decompress_error_bound, for the fused sum: P fma roundings of the
-    weighted decoded codes, then log2 B + 1 roundings in the rotation."""
+    """As decompress_error_bound, for the fused sum: each part's weighted
+    decoded code is rounded and then added (2 P roundings), then log2 B + 1
+    roundings in the rotation."""
     B = block
     P = len(parts)
     tot = None
@@ -128,6 +129,6 @@ def decompress_sum_error_bound(parts, block):
         a = np.asarray(alpha, dtype=np.float32).astype(np.float64).reshape(-1)
         w = d / (a[:, None] * np.float64(np.float32(s)))
         tot = w if tot is None else tot + w
-    k = P + np.log2(B) + 2
+    k = 2 * P + np.log2(B) + 2
     per_block = k * U32 * np.sum(tot, axis=1) / np.sqrt(B)
     return np.repeat(per_block, B)

@@ -33,7 +33,9 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["taco_compress", "taco_decompress", "taco_decompress_sum", "taco_status_string",
               "taco_num_scales", "taco_compress_workspace_bytes", "taco_version",
-              "taco_set_rotation_engine", "taco_get_rotation_engine"]:
+              "taco_set_rotation_engine", "taco_get_rotation_engine", "taco_set_single_pass",
+              "taco_get_single_pass", "taco_decompress_sum_compress",
+              "taco_decompress_sum_compress_workspace_bytes"]:
         assert n in names
 
 
@@ -51,7 +53,7 @@ def test_host_only_queries(lib):
     assert lib.taco_num_scales(0, 128, 64) == -1
     assert lib.taco_compress_workspace_bytes(4096, 4096, 128) > 0
     assert lib.taco_compress_workspace_bytes(4, 96, 64) == 0
-    for s in range(10):
+    for s in range(11):
         assert lib.taco_status_string(s).decode().startswith("TACO_")
     assert lib.taco_set_rotation_engine(7) == 9
     assert lib.taco_set_rotation_engine(1) == 9          # VALU engine switched off
@@ -86,3 +88,14 @@ def test_argument_checks_fail_before_any_launch(lib):
     nul = (ctypes.c_void_p * 1)(None)
     assert s(nul, arr, arr, 1, 8, 128, 64, FAKE, None) == 1
     assert s(arr, arr, arr, 1, 8, 128, 64, FAKE + 4, None) == 2
+    dsc = lib.taco_decompress_sum_compress
+    ws2 = lib.taco_decompress_sum_compress_workspace_bytes(8, 128, 64)
+    assert ws2 >= 2 * 8 * 128 + ws
+    assert lib.taco_decompress_sum_compress_workspace_bytes(8, 96, 64) == 0
+    other = FAKE + 0x1000
+    assert dsc(arr, arr, arr, 1, 8, 128, 64, f, FAKE, other, other, FAKE, ws2, None) == 10
+    assert dsc(arr, arr, arr, 1, 8, 128, 64, f, other, FAKE, other, FAKE, ws2, None) == 10
+    assert dsc(arr, arr, arr, 1, 8, 128, 64, f, other, other, other, FAKE, ws2 - 16, None) == 6
+    assert dsc(arr, arr, arr, 0, 8, 128, 64, f, other, other, other, FAKE, ws2, None) == 7
+    assert dsc(arr, arr, arr, 1, 8, 128, 64, ctypes.c_float(-1.0), other, other, other, FAKE, ws2, None) == 5
+    assert dsc(arr, arr, arr, 1, 8, 128, 64, f, other, None, other, FAKE, ws2, None) == 1

@@ -270,3 +270,69 @@ def test_full_size_decompress_sum_32_layers(taco):
     outs = [taco.decompress_sum(gp, 256) for _ in range(32)]
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
+
+
+# ------------------------------------------------------------------ decompress-sum-compress
+def run_decompress_sum_compress(taco, part_bits, block, E=1.0):
+    """compress(decompress_sum(parts)) in one call.
+
+    (a) Bitwise equal to the two GPU calls in sequence, each of which meets its
+    own element-wise parity bars against the oracle in the tests above.
+    (b) Against the oracle's composition directly.  The GPU's fp32 sum can round
+    to a different bf16 value than the oracle's fp64 sum, by one ulp near a
+    tie and by several where the parts cancel (the sum's error scales with the
+    sum of the parts' magnitudes, not with the result), and such an element
+    changes the rotated values of its whole block.  So the direct comparison
+    holds alpha to 1e-6 in all but 1% of blocks (2^-6 everywhere), s to 2^-7,
+    at most 1e-3 of the codes may differ, and the reconstructions must agree
+    to 1e-3 relative Frobenius."""
+    T, H = part_bits[0].shape
+    print(f"[case] decompress_sum_compress parts={len(part_bits)} shape=({T},{H}) block={block} "
+          f"single_pass={taco.get_single_pass()}", flush=True)
+    trip_o = [oracle.compress(b, block) for b in part_bits]
+    gparts = [(torch.from_numpy(q).cuda(), torch.from_numpy(a).cuda(),
+               torch.tensor([s], dtype=torch.float32).cuda()) for q, a, s in trip_o]
+    got = [t.clone() for t in taco.decompress_sum_compress(gparts, block, E)]
+    comp = taco.compress(taco.decompress_sum(gparts, block), block, E)
+    for a, b in zip(got, comp):
+        assert torch.equal(a, b)
+    q_g, a_g, s_g = gpu_triple_np(*got)
+    q_o, a_o, s_o = oracle.decompress_sum_compress(trip_o, block, E)
+    rel_a = np.abs(a_g.astype(np.float64) - a_o) / a_o
+    assert np.mean(rel_a > 1e-6) <= 0.01 and np.max(rel_a) <= 2.0 ** -6
+    rel_s = abs(float(s_g) - float(s_o)) / float(s_o)
+    assert rel_s <= 2.0 ** -7
+    if rel_s <= 1e-6:
+        assert np.mean(parity.ordinal(q_g) != parity.ordinal(q_o)) <= 1e-3
+    xh_g = W.bf16_bits(taco.decompress(*got, block))
+    xh_o = oracle.decompress(q_o, a_o, s_o, block)
+    assert parity.rel_frobenius(xh_g, xh_o) <= 1e-3
+    return got
+
+
+@pytest.mark.parametrize("nparts", [1, 2, 3, 4, 8])
+def test_decompress_sum_compress_small(taco, engine, nparts):
+    parts = [W.bf16_bits(W.make("dsum_part", seed=p, tokens=7)) for p in range(nparts)]
+    run_decompress_sum_compress(taco, parts, 256)
+
+
+@pytest.mark.parametrize("block", [64, 128])
+def test_decompress_sum_compress_other_blocks(taco, engine, block):
+    parts = [W.bf16_bits(W.make("gpt3_6p7b_act", seed=p, tokens=11)) for p in range(4)]
+    run_decompress_sum_compress(taco, parts, block, 0.5)
+
+
+def test_decompress_sum_compress_zero_sum(taco, engine):
+    bits = W.bf16_bits(W.make("gpt3_6p7b_act", seed=3, tokens=5))
+    q, a, s = oracle.compress(bits, 128)
+    neg = (q ^ np.uint8(0x80), a, s)
+    gparts = [(torch.from_numpy(t[0]).cuda(), torch.from_numpy(t[1]).cuda(),
+               torch.tensor([t[2]], dtype=torch.float32).cuda()) for t in [(q, a, s), neg]]
+    qz, az, sz = gpu_triple_np(*taco.decompress_sum_compress(gparts, 128))
+    assert sz == 1.0 and np.all(az == 1.0) and np.all(parity.ordinal(qz) == 0)
+
+
+def test_full_size_decompress_sum_compress(taco, engine):
+    """The decompress-sum workload (4 parts of [4096, 4096], block 256)."""
+    parts = [W.bf16_bits(W.make("dsum_part", seed=p)) for p in range(4)]
+    run_decompress_sum_compress(taco, parts, 256)

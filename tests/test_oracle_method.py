@@ -243,6 +243,25 @@ def test_decompress_sum_identities():
         oracle.decompress_sum([], 128)
 
 
+def test_decompress_sum_compress_is_the_composition_and_closed_forms():
+    x1, x2 = small_mix(8, 512, 31), small_mix(8, 512, 32)
+    p1, p2 = oracle.compress(x1, 128), oracle.compress(x2, 128)
+    q, a, s = oracle.decompress_sum_compress([p1, p2], 128)
+    q2, a2, s2 = oracle.compress(oracle.decompress_sum([p1, p2], 128), 128)
+    assert np.array_equal(q, q2) and np.array_equal(a, a2) and s == s2
+    # the two-shot round trip stays close to the exact fp64 sum of the inputs
+    exact = f64_of(x1) + f64_of(x2)
+    back = oracle.decompress_f64(q, a, s, 128)
+    assert np.linalg.norm(back - exact) <= 0.08 * np.linalg.norm(exact)
+    # a part and its negation sum to zero: the zero tensor's closed form
+    neg = (p1[0] ^ np.uint8(0x80), p1[1], p1[2])
+    qz, az, sz = oracle.decompress_sum_compress([p1, neg], 128)
+    assert sz == 1.0 and np.all(az == 1.0) and np.all(qz == 0)
+    # the target energy is a gauge here too: same codes, alpha scaled by sqrt(E)
+    q4, a4, s4 = oracle.decompress_sum_compress([p1, p2], 128, 4.0)
+    assert np.array_equal(q4, q) and np.allclose(a4, 2 * a, rtol=2 ** -22)
+
+
 def test_shape_and_argument_checks():
     x = np.zeros((2, 96), dtype=np.uint16)
     with pytest.raises(ValueError):
