@@ -147,10 +147,15 @@ def main():
             "s": [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(2)],
             "xh": [torch.empty((TOKENS, HIDDEN), dtype=torch.bfloat16, device=dev) for _ in range(2)],
             "sum": torch.empty((TOKENS, HIDDEN), dtype=torch.bfloat16, device=dev),
+            "rq": torch.empty((TOKENS, HIDDEN), dtype=torch.uint8, device=dev),
+            "ra": torch.empty((TOKENS, HIDDEN // BLOCK), dtype=torch.float32, device=dev),
+            "rs": torch.empty(1, dtype=torch.float32, device=dev),
         }
         sets.append(s)
     del act, grad, part_src
     ws = torch.zeros(taco.workspace_bytes(TOKENS, HIDDEN, BLOCK), dtype=torch.uint8, device=dev)
+    ws_rs = torch.zeros(taco.load().taco_decompress_sum_compress_workspace_bytes(TOKENS, HIDDEN, BLOCK),
+                        dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     taco.set_single_pass(args.single_pass == "on")
     if args.copy_probe_mib > 0:
@@ -176,6 +181,10 @@ def main():
     def op_sum(st):
         taco.decompress_sum(st["parts"], BLOCK, out=st["sum"])
 
+    def op_sum_compress(st):
+        taco.decompress_sum_compress(st["parts"], BLOCK, q=st["rq"], alpha=st["ra"], scale=st["rs"],
+                                     workspace=ws_rs)
+
     def step(st):
         for k in range(2):
             op_compress(st, k)
@@ -199,6 +208,7 @@ def main():
         "compress": (capture(lambda: [op_compress(st, k) for st in sets for k in range(2)]), 2 * len(sets)),
         "decompress": (capture(lambda: [op_decompress(st, k) for st in sets for k in range(2)]), 2 * len(sets)),
         "decompress_sum": (capture(lambda: [op_sum(st) for st in sets]), len(sets)),
+        "decompress_sum_compress": (capture(lambda: [op_sum_compress(st) for st in sets]), len(sets)),
     }
     for g in step_graphs:
         g.replay()
@@ -222,7 +232,7 @@ def main():
     # ---- per-op timed regions: average duration of one call of each op
     reps = max(1, args.steps // 4)
     avg_us = {}
-    for op in ops:
+    for op in ops + ["decompress_sum_compress"]:
         g, calls = op_graphs[op]
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -241,6 +251,7 @@ def main():
         "compress": 2 * N + N + 4 * nscales + 4,
         "decompress": N + 4 * nscales + 4 + 2 * N,
         "decompress_sum": NPARTS * (N + 4 * nscales + 4) + 2 * N,
+        "decompress_sum_compress": NPARTS * (N + 4 * nscales + 4) + N + 4 * nscales + 4,
     }
     achieved = alg["compress"] / (avg_us["compress"] * 1e-6) / 1e9
     traffic = measured_traffic()
@@ -285,6 +296,14 @@ def main():
                  "algorithmic_GBps": round(alg[op] / (avg_us[op] * 1e-6) / 1e9, 1),
                  "hbm_frac": round(alg[op] / (avg_us[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
             for op in ops
+        },
+        "extra_ops": {
+            "decompress_sum_compress": {
+                "avg_us": round(avg_us["decompress_sum_compress"], 3),
+                "algorithmic_GBps": round(alg["decompress_sum_compress"] / (avg_us["decompress_sum_compress"] * 1e-6) / 1e9, 1),
+                "hbm_frac": round(alg["decompress_sum_compress"] / (avg_us["decompress_sum_compress"] * 1e-6) / 1e9
+                                  / HBM_PEAK_GBS, 4),
+                "note": "4 parts -> FP8 of their bf16 sum (not part of the step)"},
         },
         "wall_s_timed": round(t_wall, 4),
         "timing": "step = one HIP-graph replay of the 5 calls; per-op figures from graphs of back-to-back "
