@@ -16,6 +16,7 @@ import torch
 from .build import LIB_PATH
 
 TACO_MAX_PARTS = 8
+TACO_AMAX_SLOTS = 64
 _STATUS = {
     0: "TACO_OK", 1: "TACO_ERR_NULL", 2: "TACO_ERR_ALIGN", 3: "TACO_ERR_SHAPE",
     4: "TACO_ERR_UNSUPPORTED_BLOCK", 5: "TACO_ERR_BAD_ENERGY", 6: "TACO_ERR_WORKSPACE",
@@ -85,6 +86,13 @@ def load() -> ctypes.CDLL:
                                                      ctypes.POINTER(_vp), _i32, _i64, _i64, _i32,
                                                      ctypes.c_float, _vp, _vp, _vp, _vp,
                                                      ctypes.c_size_t, _vp]
+        lib.taco_compress_blockscale.restype = ctypes.c_int
+        lib.taco_compress_blockscale.argtypes = [_vp, _i64, _i64, _i32, ctypes.c_float, _vp, _vp, _vp, _vp]
+        lib.taco_decompress_blockscale.restype = ctypes.c_int
+        lib.taco_decompress_blockscale.argtypes = [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
+        lib.taco_compress_delayed.restype = ctypes.c_int
+        lib.taco_compress_delayed.argtypes = [_vp, _i64, _i64, _i32, ctypes.c_float, _vp, _vp, _vp, _vp,
+                                              _vp, _vp]
         lib.taco_decompress_sum.restype = ctypes.c_int
         lib.taco_decompress_sum.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                             ctypes.POINTER(_vp), _i32, _i64, _i64, _i32, _vp, _vp]
@@ -324,3 +332,83 @@ def decompress_sum(parts, block: int, *, out: torch.Tensor | None = None,
     sa = (_vp * P)(*[s.data_ptr() for _, _, s in parts])
     _check(lib.taco_decompress_sum(qa, aa, sa, P, T, H, block, _ptr(out), _stream(dev, stream)))
     return out
+
+
+def _compress_outputs(x, block, q, alpha, scale, per_block_scale):
+    lib = load()
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    dev = _require_gpu(x)
+    T, H = x.shape
+    n = lib.taco_num_scales(T, H, block)
+    if n < 0:
+        _check(4 if block not in (64, 128, 256) else 3)
+    if q is None:
+        q = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    if alpha is None:
+        alpha = torch.empty((T, H // block), dtype=torch.float32, device=dev)
+    if scale is None:
+        scale = torch.empty((T, H // block) if per_block_scale else (1,), dtype=torch.float32, device=dev)
+    _require_gpu(x, q, alpha, scale)
+    _require_buffer(q, "q", torch.uint8, T * H, (T, H))
+    _require_buffer(alpha, "alpha", torch.float32, n)
+    _require_buffer(scale, "scale", torch.float32, n if per_block_scale else 1)
+    return lib, dev, T, H, q, alpha, scale
+
+
+def compress_blockscale(x: torch.Tensor, block: int, target_energy: float = 1.0, *,
+                        q: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
+                        scale: torch.Tensor | None = None, stream=None):
+    """Dual-Scale variant with a per-block overflow guard: returns (q, alpha,
+    scale [tokens, hidden/block]); one streaming kernel."""
+    x = x.contiguous()
+    lib, dev, T, H, q, alpha, scale = _compress_outputs(x, block, q, alpha, scale, True)
+    _check(lib.taco_compress_blockscale(_ptr(x), T, H, block, float(target_energy), _ptr(q), _ptr(alpha),
+                                        _ptr(scale), _stream(dev, stream)))
+    return q, alpha, scale
+
+
+def decompress_blockscale(q: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, block: int, *,
+                          out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Inverse of compress_blockscale (one post-rotation scale per block)."""
+    lib = load()
+    if q.dim() != 2 or q.dtype != torch.uint8:
+        raise ValueError("q must be a 2-D uint8 tensor")
+    if alpha.dtype != torch.float32 or scale.dtype != torch.float32:
+        raise ValueError("alpha and scale must be float32")
+    dev = _require_gpu(q, alpha, scale)
+    T, H = q.shape
+    n = max(lib.taco_num_scales(T, H, block), 0)
+    if alpha.numel() != n or scale.numel() != n:
+        raise ValueError("alpha and scale need one element per block")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _require_gpu(q, out)
+    _require_buffer(out, "out", torch.bfloat16, T * H, (T, H))
+    _check(lib.taco_decompress_blockscale(_ptr(q.contiguous()), _ptr(alpha.contiguous()),
+                                          _ptr(scale.contiguous()), T, H, block, _ptr(out),
+                                          _stream(dev, stream)))
+    return out
+
+
+def compress_delayed(x: torch.Tensor, block: int, amax_prev: torch.Tensor | None = None,
+                     target_energy: float = 1.0, *, q: torch.Tensor | None = None,
+                     alpha: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                     amax_out: torch.Tensor | None = None, stream=None):
+    """Dual-Scale variant with the per-tensor scale of an earlier tensor:
+    s = 448 / max(amax_prev) (1 if zero).  Returns (q, alpha, scale, amax_out),
+    where amax_out (TACO_AMAX_SLOTS fp32; zero-filled when not passed) holds
+    this tensor's largest |y| as its maximum, to pass as amax_prev next time.
+    Decompress with decompress()."""
+    x = x.contiguous()
+    lib, dev, T, H, q, alpha, scale = _compress_outputs(x, block, q, alpha, scale, False)
+    if amax_prev is None:
+        amax_prev = torch.zeros(TACO_AMAX_SLOTS, dtype=torch.float32, device=dev)
+    if amax_out is None:
+        amax_out = torch.zeros(TACO_AMAX_SLOTS, dtype=torch.float32, device=dev)
+    for t, name in ((amax_prev, "amax_prev"), (amax_out, "amax_out")):
+        _require_gpu(x, t)
+        _require_buffer(t, name, torch.float32, TACO_AMAX_SLOTS)
+    _check(lib.taco_compress_delayed(_ptr(x), T, H, block, float(target_energy), _ptr(amax_prev), _ptr(q),
+                                     _ptr(alpha), _ptr(scale), _ptr(amax_out), _stream(dev, stream)))
+    return q, alpha, scale, amax_out

@@ -728,19 +728,21 @@ __device__ __forceinline__ void rotate_f32(float (&v)[NA][8], const Quad& qd) {
 // moves 32 contiguous bytes of codes per quad, one store 64 contiguous bytes
 // of bf16 (staging through LDS measured slower here).  Each wavefront first
 // issues the loads of all U of its tiles, then decodes, rotates and stores.
-template <int B, int U>
+// SBLK: `scale` holds one post-rotation scale per block (the per-block
+// Dual-Scale variant) instead of one per tensor.
+template <int B, int U, bool SBLK>
 __global__ __launch_bounds__(kThreads) void decompress_kernel(
     const uint2* __restrict__ q, const float* __restrict__ alpha, const float* __restrict__ scale,
     int64_t nblocks, uint4* __restrict__ out) {
   constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16;
   const Quad qd;
-  const float s = *scale;
+  const float s = SBLK ? 1.0f : *scale;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
   for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
        t0 += W * U) {
     uint2 raw[U][NA];
-    float al[U];
+    float al[U], sk[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t k = (t0 + u * W) * kTileBlocks + qd.blk;
@@ -749,6 +751,7 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
       for (int a = 0; a < NA; ++a)
         raw[u][a] = ok ? load8<TACO_NT_Q_LOADS != 0>(&q[k * C16 + 4 * a + qd.ql]) : make_uint2(0, 0);
       al[u] = ok ? alpha[k] : 1.0f;
+      sk[u] = SBLK ? (ok ? scale[k] : 1.0f) : s;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -758,7 +761,7 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
 #pragma unroll
       for (int a = 0; a < NA; ++a) from_fp8x8(raw[u][a], v[a]);
       rotate_f32<NA>(v, qd);
-      const float r = (Blk<B>::rsqrt_b / (al[u] * s)) * qd.debt;
+      const float r = (Blk<B>::rsqrt_b / (al[u] * sk[u])) * qd.debt;
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         const uint4 o = to_bf16x8(v[a], r);
@@ -997,6 +1000,97 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
   }
 }
 
+// ============================================================== single-pass Dual-Scale variants
+//
+// Dual-Scale variants whose scales need no tensor-wide maximum, so that
+// compression is one streaming kernel without a grid-wide barrier, the single
+// fused kernel the pages describe [TACO pt-summary, 2.B.2 and 2.B.3]:
+//   kDsBlockGuard  a per-block post-rotation scale, s_k = 448 / max|y_k| when
+//                  the block would overflow and 1 otherwise, stored per block;
+//   kDsDelayed     the per-tensor s = 448 / amax_prev of an earlier tensor,
+//                  rotated values beyond the range saturating at +-448; this
+//                  tensor's maximum is folded into kAmaxSlots words of amax_out
+//                  (atomic max at slot workgroup mod kAmaxSlots, spreading the
+//                  atomics over separate lines) for the next call.
+// One tile per wavefront; the arithmetic per tile is the per-tensor path's
+// (MFMA rotation of raw x, alpha from the same registers).
+constexpr int kDsBlockGuard = 1;
+constexpr int kDsDelayed = 2;
+constexpr int kAmaxSlots = TACO_AMAX_SLOTS;
+
+// Max over the 4 lanes of an MFMA column (lanes n, n+16, n+32, n+48): every
+// lane of the column gets it.
+__device__ __forceinline__ float column_max(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(p32[0]), __uint_as_float(p32[1]));
+  const unsigned w = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(p16[0]), __uint_as_float(p16[1]));
+}
+
+template <int B, int MODE>
+__global__ __launch_bounds__(kThreads) void compress_streaming_kernel(
+    const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb, const float* __restrict__ amax_prev,
+    float* __restrict__ alpha, float* __restrict__ scale, unsigned* __restrict__ amax_out,
+    uint4* __restrict__ q) {
+  constexpr int NK = B / 32, NM = B / 16, SROW = Blk<B>::kCodeRowMfma;
+  __shared__ float red[kWaves];
+  __shared__ __attribute__((aligned(16))) char lds_all[kWaves][kTileBlocks * SROW];
+  char* lds = lds_all[threadIdx.x >> 6];
+  const HadFrag F = make_hadamard_fragments();
+  const int lane = threadIdx.x & 63, n = lane & 15;
+  const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  const int64_t tc = t < ntiles ? t : ntiles - 1;
+  const int rv = rows_valid(tc, nblocks);
+  const int row = n < rv ? n : rv - 1;
+  uint4 xr[NK];
+  load_tile_mfma<B, true>(x, tc, nblocks, xr);
+  float s = 1.0f;
+  if constexpr (MODE == kDsDelayed) {
+    static_assert(kAmaxSlots == 64, "one amax slot per lane");
+    const float prev = wave_max(amax_prev[lane]);
+    s = prev > 0.0f ? kQmax / prev : 1.0f;
+  }
+  const float al = ash_scale(column_sum_squares<B>(xr), sqrt_eb);
+  alpha[tc * kTileBlocks + row] = al;              // duplicates write identical values
+  f32x4_t y[NM];
+  float m = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < NM; ++mt) {
+    y[mt] = hadamard_mtile<B>(F, xr, mt);
+    m = fmaxf(fmaxf(m, fabsf(y[mt][0])), fabsf(y[mt][1]));
+    m = fmaxf(fmaxf(m, fabsf(y[mt][2])), fabsf(y[mt][3]));
+  }
+  const float bmax = column_max(m) * (al * Blk<B>::rsqrt_b);     // max |y| of the block
+  if constexpr (MODE == kDsBlockGuard) {
+    s = bmax > kQmax ? kQmax / bmax : 1.0f;
+    scale[tc * kTileBlocks + row] = s;
+  }
+  const float c = (al * s) * Blk<B>::rsqrt_b;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < NM; ++mt) {
+    // saturate before the conversion
+    const float v0 = fminf(fmaxf(y[mt][0] * c, -kQmax), kQmax), v1 = fminf(fmaxf(y[mt][1] * c, -kQmax), kQmax);
+    const float v2 = fminf(fmaxf(y[mt][2] * c, -kQmax), kQmax), v3 = fminf(fmaxf(y[mt][3] * c, -kQmax), kQmax);
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    wd = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, wd, true);
+    *reinterpret_cast<int*>(lds + n * SROW + 16 * mt + 4 * g) = wd;
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (t < ntiles) lds_store_tile_to_global<B, SROW, TACO_NT_CODE_STORES != 0>(lds, q, t, rv);
+  __builtin_amdgcn_wave_barrier();
+  if constexpr (MODE == kDsDelayed) {
+    const float wg = workgroup_max<kWaves>(t < ntiles && n < rv ? bmax : 0.0f, red);
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_max(&amax_out[blockIdx.x % kAmaxSlots], __float_as_uint(wg), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+  }
+}
+
 // ----------------------------------------------------------------- host side
 
 int device_cu_count() {
@@ -1102,10 +1196,10 @@ void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, f
                      xv, nblocks, sqrt_eb, partial, gs, scale, qv);
 }
 
-template <int B>
+template <int B, bool SBLK>
 void launch_decompress(const uint8_t* q, const float* alpha, const float* scale, int64_t nblocks,
                        void* out, hipStream_t stream) {
-  hipLaunchKernelGGL((decompress_kernel<B, 1>), dim3(tile_grid(nblocks)), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((decompress_kernel<B, 1, SBLK>), dim3(tile_grid(nblocks)), dim3(kThreads), 0, stream,
                      reinterpret_cast<const uint2*>(q), alpha, scale, nblocks,
                      static_cast<uint4*>(out));
 }
@@ -1175,6 +1269,16 @@ void launch_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblo
   void* sum = ws + kCompressWorkspace;
   launch_decompress_sum<B>(parts, nparts, nblocks, sum, stream);
   launch_compress<B>(sum, nblocks, energy, q, alpha, scale, workspace, stream);
+}
+
+template <int B, int MODE>
+void launch_compress_streaming(const void* x, int64_t nblocks, float energy, const float* amax_prev,
+                               uint8_t* q, float* alpha, float* scale, float* amax_out,
+                               hipStream_t stream) {
+  const float sqrt_eb = static_cast<float>(sqrt(static_cast<double>(energy) * B));
+  hipLaunchKernelGGL((compress_streaming_kernel<B, MODE>), dim3(tile_grid(nblocks)), dim3(kThreads), 0,
+                     stream, static_cast<const uint4*>(x), nblocks, sqrt_eb, amax_prev, alpha, scale,
+                     reinterpret_cast<unsigned*>(amax_out), reinterpret_cast<uint4*>(q));
 }
 
 }  // namespace
@@ -1262,9 +1366,9 @@ taco_status_t taco_decompress(const uint8_t* q_fp8, const float* alpha, const fl
   const int64_t nblocks = tokens * (hidden / block);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (block) {
-    case 64: launch_decompress<64>(q_fp8, alpha, scale, nblocks, y_bf16, s); break;
-    case 128: launch_decompress<128>(q_fp8, alpha, scale, nblocks, y_bf16, s); break;
-    default: launch_decompress<256>(q_fp8, alpha, scale, nblocks, y_bf16, s); break;
+    case 64: launch_decompress<64, false>(q_fp8, alpha, scale, nblocks, y_bf16, s); break;
+    case 128: launch_decompress<128, false>(q_fp8, alpha, scale, nblocks, y_bf16, s); break;
+    default: launch_decompress<256, false>(q_fp8, alpha, scale, nblocks, y_bf16, s); break;
   }
   return launched();
 }
@@ -1335,6 +1439,67 @@ taco_status_t taco_decompress_sum_compress(const uint8_t* const* q_fp8, const fl
     case 64: launch_decompress_sum_compress<64>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s); break;
     case 128: launch_decompress_sum_compress<128>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s); break;
     default: launch_decompress_sum_compress<256>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s); break;
+  }
+  return launched();
+}
+
+taco_status_t taco_compress_blockscale(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,
+                                       float target_energy, uint8_t* q_fp8, float* alpha,
+                                       float* scale_blk, taco_stream_t stream) {
+  if (!x_bf16 || !q_fp8 || !alpha || !scale_blk) return TACO_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q_fp8, 16) || !aligned(alpha, 4) || !aligned(scale_blk, 4))
+    return TACO_ERR_ALIGN;
+  const taco_status_t st = check_shape(tokens, hidden, block);
+  if (st != TACO_OK) return st;
+  if (!(target_energy >= kMinEnergy && target_energy <= kMaxEnergy)) return TACO_ERR_BAD_ENERGY;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  const int64_t nblocks = tokens * (hidden / block);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (block) {
+    case 64: launch_compress_streaming<64, kDsBlockGuard>(x_bf16, nblocks, target_energy, nullptr, q_fp8, alpha, scale_blk, nullptr, s); break;
+    case 128: launch_compress_streaming<128, kDsBlockGuard>(x_bf16, nblocks, target_energy, nullptr, q_fp8, alpha, scale_blk, nullptr, s); break;
+    default: launch_compress_streaming<256, kDsBlockGuard>(x_bf16, nblocks, target_energy, nullptr, q_fp8, alpha, scale_blk, nullptr, s); break;
+  }
+  return launched();
+}
+
+taco_status_t taco_decompress_blockscale(const uint8_t* q_fp8, const float* alpha, const float* scale_blk,
+                                         int64_t tokens, int64_t hidden, int32_t block, void* y_bf16,
+                                         taco_stream_t stream) {
+  if (!q_fp8 || !alpha || !scale_blk || !y_bf16) return TACO_ERR_NULL;
+  const taco_status_t st = check_shape(tokens, hidden, block);
+  if (st != TACO_OK) return st;
+  if (!aligned(q_fp8, 16) || !aligned(y_bf16, 16) || !aligned(alpha, 4) || !aligned(scale_blk, 4))
+    return TACO_ERR_ALIGN;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  const int64_t nblocks = tokens * (hidden / block);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (block) {
+    case 64: launch_decompress<64, true>(q_fp8, alpha, scale_blk, nblocks, y_bf16, s); break;
+    case 128: launch_decompress<128, true>(q_fp8, alpha, scale_blk, nblocks, y_bf16, s); break;
+    default: launch_decompress<256, true>(q_fp8, alpha, scale_blk, nblocks, y_bf16, s); break;
+  }
+  return launched();
+}
+
+taco_status_t taco_compress_delayed(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,
+                                    float target_energy, const float* amax_prev, uint8_t* q_fp8,
+                                    float* alpha, float* scale, float* amax_out, taco_stream_t stream) {
+  if (!x_bf16 || !amax_prev || !q_fp8 || !alpha || !scale || !amax_out) return TACO_ERR_NULL;
+  if (!aligned(x_bf16, 16) || !aligned(q_fp8, 16) || !aligned(alpha, 4) || !aligned(scale, 4) ||
+      !aligned(amax_prev, 4) || !aligned(amax_out, 4))
+    return TACO_ERR_ALIGN;
+  if (amax_prev == amax_out) return TACO_ERR_ALIAS;
+  const taco_status_t st = check_shape(tokens, hidden, block);
+  if (st != TACO_OK) return st;
+  if (!(target_energy >= kMinEnergy && target_energy <= kMaxEnergy)) return TACO_ERR_BAD_ENERGY;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  const int64_t nblocks = tokens * (hidden / block);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  switch (block) {
+    case 64: launch_compress_streaming<64, kDsDelayed>(x_bf16, nblocks, target_energy, amax_prev, q_fp8, alpha, scale, amax_out, s); break;
+    case 128: launch_compress_streaming<128, kDsDelayed>(x_bf16, nblocks, target_energy, amax_prev, q_fp8, alpha, scale, amax_out, s); break;
+    default: launch_compress_streaming<256, kDsDelayed>(x_bf16, nblocks, target_energy, amax_prev, q_fp8, alpha, scale, amax_out, s); break;
   }
   return launched();
 }

@@ -78,6 +78,7 @@ typedef enum {
 } taco_engine_t;
 
 #define TACO_MAX_PARTS 8
+#define TACO_AMAX_SLOTS 64
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* taco_status_string(taco_status_t status);
@@ -189,6 +190,45 @@ taco_status_t taco_decompress_sum_compress(const uint8_t* const* q_fp8, const fl
                                            float* alpha_out, float* scale_out,
                                            void* workspace, size_t workspace_bytes,
                                            taco_stream_t stream);
+
+/*
+ * Single-pass Dual-Scale variants [TACO pt-summary, sections 2.B.2 (two scales
+ * per block; the post-rotation scale keeps values inside the FP8 range) and
+ * 2.B.3 (one fused kernel)].  Neither needs a tensor-wide maximum before
+ * writing codes, so each is one streaming kernel with no workspace and no
+ * residency requirement.
+ *
+ * Per-block overflow guard: alpha_k as in taco_compress; the post-rotation
+ * scale is per block, s_k = 448 / max|y_k| when the block's rotated values
+ * would exceed the FP8 range and 1 otherwise, so the target energy sets where
+ * the values sit in the E4M3 range.
+ *   scale_blk  out: fp32 [tokens, hidden / block], one s_k per block
+ * taco_decompress_blockscale inverts it (scale_blk in place of the per-tensor
+ * scale).
+ */
+taco_status_t taco_compress_blockscale(const void* x_bf16, int64_t tokens, int64_t hidden,
+                                       int32_t block, float target_energy, uint8_t* q_fp8,
+                                       float* alpha, float* scale_blk, taco_stream_t stream);
+taco_status_t taco_decompress_blockscale(const uint8_t* q_fp8, const float* alpha,
+                                         const float* scale_blk, int64_t tokens, int64_t hidden,
+                                         int32_t block, void* y_bf16, taco_stream_t stream);
+
+/*
+ * Delayed per-tensor scale: s = 448 / amax_prev, where amax_prev is the
+ * largest rotated value of an earlier tensor (1 if it is 0); rotated values
+ * beyond the range saturate at +-448.  Decompress with taco_decompress.
+ *   amax_prev  in : device, TACO_AMAX_SLOTS fp32; the earlier call's amax_out
+ *                   (its maximum is used; all zeros means no history)
+ *   scale      out: device fp32 [1], the s used
+ *   amax_out   in/out: device, TACO_AMAX_SLOTS fp32; each slot becomes the max
+ *                   of its content and part of this tensor's block maxima, so
+ *                   zero-filled on entry it holds this tensor's largest |y| as
+ *                   the max over the slots.  May not be amax_prev (TACO_ERR_ALIAS).
+ */
+taco_status_t taco_compress_delayed(const void* x_bf16, int64_t tokens, int64_t hidden,
+                                    int32_t block, float target_energy, const float* amax_prev,
+                                    uint8_t* q_fp8, float* alpha, float* scale, float* amax_out,
+                                    taco_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,11 @@ from .taco_oracle import (  # noqa: F401
     bf16_bits_to_f64,
     block_energy,
     compress,
+    compress_blockscale,
+    compress_delayed,
     decompress,
+    decompress_blockscale,
+    decompress_blockscale_f64,
     decompress_f64,
     decompress_sum,
     decompress_sum_compress,

@@ -268,3 +268,86 @@ def decompress_sum_compress(parts, block: int, target_energy: float = 1.0):
     other bf16 tensor (its own alpha and per-tensor s).  So this is the
     composition of the two steps, and it is pinned by their pins."""
     return compress(decompress_sum(parts, block), block, target_energy)
+
+
+# ---------------------------------------------------------------------------
+# Dual-Scale variants without a tensor-wide dependency [TACO pt-summary, 2.B.2:
+# a post-rotation scale that keeps the rotated values inside the FP8 range;
+# 2.B.3: one fused kernel]
+# ---------------------------------------------------------------------------
+
+def compress_blockscale(x_bits: np.ndarray, block: int, target_energy: float = 1.0):
+    """DS with a per-block post-rotation scale that only guards overflow.
+
+    Reading: pt-summary 2.B.2 gives every block two scalars, the pre-rotation
+    alpha_k and a post-rotation scale that makes the rotated values fit the
+    FP8 range.  After ASH a block's rotated values already sit around sqrt(E);
+    this variant scales a block down only when it would overflow:
+    s_k = fp32(448 / max|y_k|) if max|y_k| > 448, else 1.  Unlike the
+    per-tensor reading it needs no tensor-wide maximum, and E sets where the
+    values sit in the E4M3 range.
+
+    Returns (q uint8 [T, H], alpha float32 [T, H/block], s float32 [T, H/block]).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, H = x_bits.shape
+    _check_shape(T, H, block)
+    E = float(np.float32(target_energy))
+    if not (np.isfinite(E) and E > 0):
+        raise ValueError("target energy must be finite and > 0")
+    xb = bf16_bits_to_f64(x_bits).reshape(-1, block)
+    alpha = ash_scale(block_energy(xb), E)
+    y = hadamard_rotate(xb, alpha)
+    m = np.max(np.abs(y), axis=1)
+    with np.errstate(divide="ignore"):
+        s = np.where(m > Q_MAX, (Q_MAX / np.where(m > 0, m, 1.0)).astype(np.float32), np.float32(1.0))
+    s = s.astype(np.float32)
+    q = e4m3_encode(s.astype(np.float64)[:, None] * y)
+    return q.reshape(T, H), alpha.reshape(T, H // block), s.reshape(T, H // block)
+
+
+def decompress_blockscale_f64(q: np.ndarray, alpha: np.ndarray, s_blk: np.ndarray, block: int) -> np.ndarray:
+    """Unrounded (1/alpha_k) * H_B (dec(q_k) / s_k) / sqrt(B), fp64 [T, H]."""
+    q = np.asarray(q, dtype=np.uint8)
+    T, H = q.shape
+    _check_shape(T, H, block)
+    s = np.asarray(s_blk, dtype=np.float32).astype(np.float64).reshape(-1)
+    d = e4m3_decode(q).reshape(-1, block) / s[:, None]
+    h = d @ hadamard(block).T / np.sqrt(np.float64(block))
+    a = np.asarray(alpha, dtype=np.float32).astype(np.float64).reshape(-1)
+    return (h / a[:, None]).reshape(T, H)
+
+
+def decompress_blockscale(q: np.ndarray, alpha: np.ndarray, s_blk: np.ndarray, block: int) -> np.ndarray:
+    """decompress_blockscale_f64 rounded once to bf16 (uint16 patterns)."""
+    return f64_to_bf16_bits(decompress_blockscale_f64(q, alpha, s_blk, block))
+
+
+def compress_delayed(x_bits: np.ndarray, block: int, target_energy: float, amax_prev: float):
+    """DS with a per-tensor scale taken from an earlier tensor's maximum.
+
+    Reading: the per-tensor s of 2.B.2 (zh-news, method section) computed from
+    amax_prev, the largest |y| of the previous call on the same stream of
+    tensors, instead of this tensor's own: s = fp32(448 / amax_prev) (1 if
+    amax_prev is 0).  Rotated values that outgrow it saturate at +-448.  The
+    call also returns this tensor's largest |y| (in fp64) for the next call.
+    Decompression is the ordinary one.
+
+    Returns (q uint8 [T, H], alpha float32 [T, H/block], s float32, amax float64).
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, H = x_bits.shape
+    _check_shape(T, H, block)
+    E = float(np.float32(target_energy))
+    if not (np.isfinite(E) and E > 0):
+        raise ValueError("target energy must be finite and > 0")
+    prev = float(np.float32(amax_prev))
+    if not (np.isfinite(prev) and prev >= 0):
+        raise ValueError("amax_prev must be finite and >= 0")
+    xb = bf16_bits_to_f64(x_bits).reshape(-1, block)
+    alpha = ash_scale(block_energy(xb), E)
+    y = hadamard_rotate(xb, alpha)
+    s = np.float32(Q_MAX / prev) if prev > 0 else np.float32(1.0)
+    q = quantize(y, s)
+    amax = float(np.max(np.abs(y))) if y.size else 0.0
+    return q.reshape(T, H), alpha.reshape(T, H // block), s, amax

@@ -336,3 +336,97 @@ def test_full_size_decompress_sum_compress(taco, engine):
     """The decompress-sum workload (4 parts of [4096, 4096], block 256)."""
     parts = [W.bf16_bits(W.make("dsum_part", seed=p)) for p in range(4)]
     run_decompress_sum_compress(taco, parts, 256)
+
+
+# ------------------------------------------------------------ Dual-Scale variants
+def run_blockscale(taco, bits, block, E):
+    T, H = bits.shape
+    print(f"[case] compress_blockscale shape=({T},{H}) block={block} E={E}", flush=True)
+    q_o, a_o, s_o = oracle.compress_blockscale(bits, block, E)
+    q_g, a_g, s_g = [t.cpu().numpy() for t in taco.compress_blockscale(to_gpu_bits(bits), block, E)]
+    parity.check_scales(a_g, 1.0, a_o, 1.0)
+    rel_s = np.abs(s_g.astype(np.float64) - s_o) / s_o
+    assert np.max(rel_s) <= 1e-6
+    parity.check_codes(q_g, q_o, bits, a_o, s_o, block)
+    trip = [torch.from_numpy(t).cuda() for t in (q_o, a_o, s_o)]
+    xh_g = W.bf16_bits(taco.decompress_blockscale(*trip, block))
+    xh_o = oracle.decompress_blockscale(q_o, a_o, s_o, block)
+    exact = oracle.decompress_blockscale_f64(q_o, a_o, s_o, block)
+    parity.bf16_neighbours_ok(xh_g, xh_o, exact, parity.decompress_error_bound(q_o, a_o, s_o, block),
+                              MAX_BF16_FRAC)
+    return q_g, a_g, s_g
+
+
+@pytest.mark.parametrize("E", [1.0, 2.0 ** 12, 2.0 ** 16])
+@pytest.mark.parametrize("name,tokens", [("tiny", 3), ("gpt2_1p5b", 37), ("gpt3_6p7b_act", 19),
+                                         ("dsum_part", 9)])
+def test_blockscale_small(taco, name, tokens, E):
+    w = W.WORKLOADS[name]
+    run_blockscale(taco, W.bf16_bits(W.make(name, seed=4, tokens=tokens)), w.block, E)
+
+
+def test_blockscale_overflowing_blocks_reach_448(taco):
+    bits = W.bf16_bits(W.make("gpt3_6p7b_act", seed=6, tokens=8))
+    q, a, s = run_blockscale(taco, bits, 128, 2.0 ** 16)
+    over = s.reshape(-1) < 1.0
+    assert over.any()
+    assert np.all(np.max(parity.ordinal(q).reshape(-1, 128)[over] ** 2, axis=1) == 126 ** 2)
+
+
+@pytest.mark.parametrize("name", ["gpt3_6p7b_act", "qwen_7b"])
+def test_full_size_blockscale(taco, name):
+    w = W.WORKLOADS[name]
+    run_blockscale(taco, W.bf16_bits(W.make(name, seed=0)), w.block, 1.0)
+
+
+def run_delayed(taco, bits, block, E, amax_prev_value):
+    """One delayed-scale call with amax_prev holding amax_prev_value in slot 0;
+    the oracle gets the same value."""
+    T, H = bits.shape
+    print(f"[case] compress_delayed shape=({T},{H}) block={block} amax_prev={amax_prev_value}", flush=True)
+    prev = torch.zeros(taco.TACO_AMAX_SLOTS, dtype=torch.float32, device="cuda")
+    prev[0] = amax_prev_value
+    q_o, a_o, s_o, A_o = oracle.compress_delayed(bits, block, E, amax_prev_value)
+    q_g, a_g, s_g, amax = taco.compress_delayed(to_gpu_bits(bits), block, prev, E)
+    q_g, a_g, s_g = gpu_triple_np(q_g, a_g, s_g)
+    assert s_g == s_o                           # the same fp32 division on both sides
+    parity.check_scales(a_g, s_g, a_o, s_o)
+    parity.check_codes(q_g, q_o, bits, a_o, s_o, block)
+    A_g = float(amax.max().cpu())
+    assert abs(A_g - A_o) <= 1e-6 * A_o
+    xh_g = W.bf16_bits(taco.decompress(*[torch.from_numpy(np.atleast_1d(t)).cuda()
+                                         for t in (q_g, a_g, s_g)], block))
+    xh_o = oracle.decompress(q_o, a_o, s_o, block)
+    assert parity.rel_frobenius(xh_g, xh_o) <= 1e-3
+    return A_o
+
+
+@pytest.mark.parametrize("name,tokens", [("tiny", 3), ("gpt2_1p5b", 37), ("gpt3_6p7b_grad", 21)])
+def test_delayed_small_sequence(taco, name, tokens):
+    """No history (s = 1), then the first call's maximum (the oracle's, as fp32),
+    then a quarter of it (saturation)."""
+    w = W.WORKLOADS[name]
+    bits = W.bf16_bits(W.make(name, seed=8, tokens=tokens))
+    A = run_delayed(taco, bits, w.block, 1.0, 0.0)
+    run_delayed(taco, bits, w.block, 1.0, float(np.float32(A)))
+    run_delayed(taco, bits, w.block, 1.0, float(np.float32(A / 4)))
+
+
+def test_delayed_amax_out_accumulates(taco):
+    """amax_out keeps the max of its content and this call's block maxima."""
+    bits = W.bf16_bits(W.make("tiny", seed=1, tokens=64))
+    x = to_gpu_bits(bits)
+    out = torch.full((taco.TACO_AMAX_SLOTS,), 1e30, dtype=torch.float32, device="cuda")
+    taco.compress_delayed(x, 64, None, 1.0, amax_out=out)
+    assert torch.all(out == 1e30)
+    out.zero_()
+    taco.compress_delayed(x, 64, None, 1.0, amax_out=out)
+    _, _, _, A = oracle.compress_delayed(bits, 64, 1.0, 0.0)
+    assert abs(float(out.max().cpu()) - A) <= 1e-6 * A
+
+
+def test_full_size_delayed(taco):
+    w = W.WORKLOADS["gpt3_6p7b_act"]
+    bits = W.bf16_bits(W.make("gpt3_6p7b_act", seed=0))
+    _, _, _, A = oracle.compress_delayed(bits, w.block, 1.0, 0.0)
+    run_delayed(taco, bits, w.block, 1.0, float(np.float32(A)))
