@@ -150,6 +150,7 @@ def main():
             "rq": torch.empty((TOKENS, HIDDEN), dtype=torch.uint8, device=dev),
             "ra": torch.empty((TOKENS, HIDDEN // BLOCK), dtype=torch.float32, device=dev),
             "rs": torch.empty(1, dtype=torch.float32, device=dev),
+            "sblk": torch.empty((TOKENS, HIDDEN // BLOCK), dtype=torch.float32, device=dev),
         }
         sets.append(s)
     del act, grad, part_src
@@ -181,6 +182,20 @@ def main():
     def op_sum(st):
         taco.decompress_sum(st["parts"], BLOCK, out=st["sum"])
 
+    amax = [torch.zeros(taco.TACO_AMAX_FLOATS, dtype=torch.float32, device=dev) for _ in range(2)]
+
+    def op_blockscale(st, k):
+        x = st["act"] if k == 0 else st["grad"]
+        taco.compress_blockscale(x, BLOCK, q=st["q"][k], alpha=st["a"][k], scale=st["sblk"])
+
+    def op_blockscale_dec(st, k):
+        taco.decompress_blockscale(st["q"][k], st["a"][k], st["sblk"], BLOCK, out=st["xh"][k])
+
+    def op_delayed(st, k):
+        x = st["act"] if k == 0 else st["grad"]
+        taco.compress_delayed(x, BLOCK, amax[0], q=st["q"][k], alpha=st["a"][k], scale=st["s"][k],
+                              amax_out=amax[1])
+
     def op_sum_compress(st):
         taco.decompress_sum_compress(st["parts"], BLOCK, q=st["rq"], alpha=st["ra"], scale=st["rs"],
                                      workspace=ws_rs)
@@ -209,6 +224,12 @@ def main():
         "decompress": (capture(lambda: [op_decompress(st, k) for st in sets for k in range(2)]), 2 * len(sets)),
         "decompress_sum": (capture(lambda: [op_sum(st) for st in sets]), len(sets)),
         "decompress_sum_compress": (capture(lambda: [op_sum_compress(st) for st in sets]), len(sets)),
+        "compress_blockscale": (capture(lambda: [op_blockscale(st, k) for st in sets for k in range(2)]),
+                                2 * len(sets)),
+        "decompress_blockscale": (capture(lambda: [op_blockscale_dec(st, k) for st in sets for k in range(2)]),
+                                  2 * len(sets)),
+        "compress_delayed": (capture(lambda: [op_delayed(st, k) for st in sets for k in range(2)]),
+                             2 * len(sets)),
     }
     for g in step_graphs:
         g.replay()
@@ -232,7 +253,8 @@ def main():
     # ---- per-op timed regions: average duration of one call of each op
     reps = max(1, args.steps // 4)
     avg_us = {}
-    for op in ops + ["decompress_sum_compress"]:
+    extra = ["decompress_sum_compress", "compress_blockscale", "decompress_blockscale", "compress_delayed"]
+    for op in ops + extra:
         g, calls = op_graphs[op]
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -252,6 +274,9 @@ def main():
         "decompress": N + 4 * nscales + 4 + 2 * N,
         "decompress_sum": NPARTS * (N + 4 * nscales + 4) + 2 * N,
         "decompress_sum_compress": NPARTS * (N + 4 * nscales + 4) + N + 4 * nscales + 4,
+        "compress_blockscale": 3 * N + 8 * nscales,
+        "decompress_blockscale": 3 * N + 8 * nscales,
+        "compress_delayed": 3 * N + 4 * nscales + 4,
     }
     achieved = alg["compress"] / (avg_us["compress"] * 1e-6) / 1e9
     traffic = measured_traffic()
@@ -298,13 +323,13 @@ def main():
             for op in ops
         },
         "extra_ops": {
-            "decompress_sum_compress": {
-                "avg_us": round(avg_us["decompress_sum_compress"], 3),
-                "algorithmic_GBps": round(alg["decompress_sum_compress"] / (avg_us["decompress_sum_compress"] * 1e-6) / 1e9, 1),
-                "hbm_frac": round(alg["decompress_sum_compress"] / (avg_us["decompress_sum_compress"] * 1e-6) / 1e9
-                                  / HBM_PEAK_GBS, 4),
-                "note": "4 parts -> FP8 of their bf16 sum (not part of the step)"},
+            op: {"avg_us": round(avg_us[op], 3),
+                 "algorithmic_GBps": round(alg[op] / (avg_us[op] * 1e-6) / 1e9, 1),
+                 "hbm_frac": round(alg[op] / (avg_us[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+            for op in extra
         },
+        "extra_ops_note": "not part of the step: decompress_sum_compress (4 parts -> FP8 of their bf16 "
+                          "sum), the per-block-guard and delayed-scale Dual-Scale variants",
         "wall_s_timed": round(t_wall, 4),
         "timing": "step = one HIP-graph replay of the 5 calls; per-op figures from graphs of back-to-back "
                   "calls over all buffer sets",

@@ -5,6 +5,7 @@ Python face of libtaco (include/taco.h): ``compress``, ``decompress`` and
 loaded on first use and the calls raise if it is missing; there is no CPU path.
 """
 from ._binding import (  # noqa: F401
+    TACO_AMAX_FLOATS,
     TACO_AMAX_SLOTS,
     TACO_MAX_PARTS,
     TacoError,
@@ -27,7 +28,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "TACO_AMAX_SLOTS", "TACO_MAX_PARTS", "TacoError", "compress", "compress_blockscale",
+    "TACO_AMAX_FLOATS", "TACO_AMAX_SLOTS", "TACO_MAX_PARTS", "TacoError", "compress", "compress_blockscale",
     "compress_delayed", "decompress", "decompress_blockscale", "decompress_sum", "decompress_sum_compress", "get_rotation_engine",
     "get_single_pass", "library_path", "load", "num_scales", "set_rotation_engine", "set_single_pass",
     "version", "workspace_bytes",

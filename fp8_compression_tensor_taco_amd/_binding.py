@@ -17,6 +17,7 @@ from .build import LIB_PATH
 
 TACO_MAX_PARTS = 8
 TACO_AMAX_SLOTS = 64
+TACO_AMAX_FLOATS = 4096
 _STATUS = {
     0: "TACO_OK", 1: "TACO_ERR_NULL", 2: "TACO_ERR_ALIGN", 3: "TACO_ERR_SHAPE",
     4: "TACO_ERR_UNSUPPORTED_BLOCK", 5: "TACO_ERR_BAD_ENERGY", 6: "TACO_ERR_WORKSPACE",
@@ -397,18 +398,19 @@ def compress_delayed(x: torch.Tensor, block: int, amax_prev: torch.Tensor | None
                      amax_out: torch.Tensor | None = None, stream=None):
     """Dual-Scale variant with the per-tensor scale of an earlier tensor:
     s = 448 / max(amax_prev) (1 if zero).  Returns (q, alpha, scale, amax_out),
-    where amax_out (TACO_AMAX_SLOTS fp32; zero-filled when not passed) holds
-    this tensor's largest |y| as its maximum, to pass as amax_prev next time.
+    where amax_out (zero-filled when not passed) holds
+    this tensor's largest |y| as its maximum (TACO_AMAX_FLOATS fp32; see
+    include/taco.h), to pass as amax_prev next time.
     Decompress with decompress()."""
     x = x.contiguous()
     lib, dev, T, H, q, alpha, scale = _compress_outputs(x, block, q, alpha, scale, False)
     if amax_prev is None:
-        amax_prev = torch.zeros(TACO_AMAX_SLOTS, dtype=torch.float32, device=dev)
+        amax_prev = torch.zeros(TACO_AMAX_FLOATS, dtype=torch.float32, device=dev)
     if amax_out is None:
-        amax_out = torch.zeros(TACO_AMAX_SLOTS, dtype=torch.float32, device=dev)
+        amax_out = torch.zeros(TACO_AMAX_FLOATS, dtype=torch.float32, device=dev)
     for t, name in ((amax_prev, "amax_prev"), (amax_out, "amax_out")):
         _require_gpu(x, t)
-        _require_buffer(t, name, torch.float32, TACO_AMAX_SLOTS)
+        _require_buffer(t, name, torch.float32, TACO_AMAX_FLOATS)
     _check(lib.taco_compress_delayed(_ptr(x), T, H, block, float(target_energy), _ptr(amax_prev), _ptr(q),
                                      _ptr(alpha), _ptr(scale), _ptr(amax_out), _stream(dev, stream)))
     return q, alpha, scale, amax_out

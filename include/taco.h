@@ -78,7 +78,13 @@ typedef enum {
 } taco_engine_t;
 
 #define TACO_MAX_PARTS 8
+/* amax buffers of taco_compress_delayed: TACO_AMAX_FLOATS fp32 (16 KiB) holding
+ * TACO_AMAX_SLOTS slots, one per 256-byte line at index
+ * i * (TACO_AMAX_FLOATS / TACO_AMAX_SLOTS); the other entries are never
+ * written, so when zero-filled the max over the whole buffer is the max over
+ * the slots. */
 #define TACO_AMAX_SLOTS 64
+#define TACO_AMAX_FLOATS 4096
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* taco_status_string(taco_status_t status);
@@ -217,13 +223,14 @@ taco_status_t taco_decompress_blockscale(const uint8_t* q_fp8, const float* alph
  * Delayed per-tensor scale: s = 448 / amax_prev, where amax_prev is the
  * largest rotated value of an earlier tensor (1 if it is 0); rotated values
  * beyond the range saturate at +-448.  Decompress with taco_decompress.
- *   amax_prev  in : device, TACO_AMAX_SLOTS fp32; the earlier call's amax_out
- *                   (its maximum is used; all zeros means no history)
+ *   amax_prev  in : device, TACO_AMAX_FLOATS fp32; the earlier call's amax_out
+ *                   (the max over its slots is used; all zeros means no history)
  *   scale      out: device fp32 [1], the s used
- *   amax_out   in/out: device, TACO_AMAX_SLOTS fp32; each slot becomes the max
- *                   of its content and part of this tensor's block maxima, so
- *                   zero-filled on entry it holds this tensor's largest |y| as
- *                   the max over the slots.  May not be amax_prev (TACO_ERR_ALIAS).
+ *   amax_out   in/out: device, TACO_AMAX_FLOATS fp32; each slot becomes the
+ *                   max of its content and part of this tensor's block maxima,
+ *                   so zero-filled on entry it holds this tensor's largest |y|
+ *                   as the max over the buffer.  May not be amax_prev
+ *                   (TACO_ERR_ALIAS).
  */
 taco_status_t taco_compress_delayed(const void* x_bf16, int64_t tokens, int64_t hidden,
                                     int32_t block, float target_energy, const float* amax_prev,

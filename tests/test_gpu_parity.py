@@ -384,7 +384,7 @@ def run_delayed(taco, bits, block, E, amax_prev_value):
     the oracle gets the same value."""
     T, H = bits.shape
     print(f"[case] compress_delayed shape=({T},{H}) block={block} amax_prev={amax_prev_value}", flush=True)
-    prev = torch.zeros(taco.TACO_AMAX_SLOTS, dtype=torch.float32, device="cuda")
+    prev = torch.zeros(taco.TACO_AMAX_FLOATS, dtype=torch.float32, device="cuda")
     prev[0] = amax_prev_value
     q_o, a_o, s_o, A_o = oracle.compress_delayed(bits, block, E, amax_prev_value)
     q_g, a_g, s_g, amax = taco.compress_delayed(to_gpu_bits(bits), block, prev, E)
@@ -416,7 +416,7 @@ def test_delayed_amax_out_accumulates(taco):
     """amax_out keeps the max of its content and this call's block maxima."""
     bits = W.bf16_bits(W.make("tiny", seed=1, tokens=64))
     x = to_gpu_bits(bits)
-    out = torch.full((taco.TACO_AMAX_SLOTS,), 1e30, dtype=torch.float32, device="cuda")
+    out = torch.full((taco.TACO_AMAX_FLOATS,), 1e30, dtype=torch.float32, device="cuda")
     taco.compress_delayed(x, 64, None, 1.0, amax_out=out)
     assert torch.all(out == 1e30)
     out.zero_()
