@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     get_single_pass,
     set_rotation_engine,
     set_single_pass,
+    two_shot_allreduce,
     decompress,
     decompress_blockscale,
     decompress_sum,
@@ -30,6 +31,6 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "TACO_AMAX_FLOATS", "TACO_AMAX_SLOTS", "TACO_MAX_PARTS", "TacoError", "compress", "compress_blockscale",
     "compress_delayed", "decompress", "decompress_blockscale", "decompress_sum", "decompress_sum_compress", "get_rotation_engine",
-    "get_single_pass", "library_path", "load", "num_scales", "set_rotation_engine", "set_single_pass",
+    "get_single_pass", "library_path", "load", "num_scales", "set_rotation_engine", "set_single_pass", "two_shot_allreduce",
     "version", "workspace_bytes",
 ]

@@ -414,3 +414,27 @@ def compress_delayed(x: torch.Tensor, block: int, amax_prev: torch.Tensor | None
     _check(lib.taco_compress_delayed(_ptr(x), T, H, block, float(target_energy), _ptr(amax_prev), _ptr(q),
                                      _ptr(alpha), _ptr(scale), _ptr(amax_out), _stream(dev, stream)))
     return q, alpha, scale, amax_out
+
+
+def two_shot_allreduce(xs, block: int, target_energy: float = 1.0, stream=None) -> torch.Tensor:
+    """The compressed two-shot all-reduce of P bf16 [T, H] tensors as P ranks
+    would run it, emulated on one GPU with the library's calls: each rank's
+    compress; per row shard j (T/P whole rows), decompress_sum_compress over
+    the ranks' rows of that shard (the reduce-scatter step, FP8 out for the
+    all-gather); decompress of every reduced shard.  Returns the bf16 result."""
+    xs = [x.contiguous() for x in xs]
+    P = len(xs)
+    if P < 1 or P > TACO_MAX_PARTS:
+        _check(7)
+    T, H = xs[0].shape
+    if T % P != 0 or any(x.shape != (T, H) for x in xs):
+        raise ValueError("P tensors of one shape whose rows split into P equal shards")
+    rows = T // P
+    comp = [compress(x, block, target_energy, stream=stream) for x in xs]
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=xs[0].device)
+    for j in range(P):
+        sl = slice(j * rows, (j + 1) * rows)
+        red = decompress_sum_compress([(q[sl], a[sl], s) for q, a, s in comp], block, target_energy,
+                                      stream=stream)
+        decompress(*red, block, out=out[sl], stream=stream)
+    return out

@@ -26,4 +26,5 @@ from .taco_oracle import (  # noqa: F401
     hadamard,
     hadamard_rotate,
     quantize,
+    two_shot_allreduce,
 )

@@ -351,3 +351,32 @@ def compress_delayed(x_bits: np.ndarray, block: int, target_energy: float, amax_
     q = quantize(y, s)
     amax = float(np.max(np.abs(y))) if y.size else 0.0
     return q.reshape(T, H), alpha.reshape(T, H // block), s, amax
+
+
+def two_shot_allreduce(xs_bits, block: int, target_energy: float = 1.0):
+    """The compressed two-shot all-reduce of P tensors as P ranks would run it
+    [TACO pt-summary, 2.B.3: reduce-scatter then all-gather, compression on
+    both legs], emulated on one device: every rank compresses its tensor; the
+    rows are split into P equal shards (whole rows, so every block stays in
+    one shard) and shard j is reduced by decompress_sum_compress over the P
+    ranks' rows of that shard, each with its rank's per-tensor scale; every
+    rank then decompresses every reduced shard.
+
+    Returns (bf16 patterns [T, H] of the all-reduced tensor, the P reduced
+    shards as (q, alpha, s))."""
+    xs_bits = [np.asarray(x, dtype=np.uint16) for x in xs_bits]
+    P = len(xs_bits)
+    T, H = xs_bits[0].shape
+    if P < 1 or T % P != 0 or any(x.shape != (T, H) for x in xs_bits):
+        raise ValueError("P tensors of one shape whose rows split into P equal shards")
+    rows = T // P
+    comp = [compress(x, block, target_energy) for x in xs_bits]
+    shards = []
+    out = np.empty((T, H), dtype=np.uint16)
+    for j in range(P):
+        sl = slice(j * rows, (j + 1) * rows)
+        parts = [(q[sl], a[sl], s) for q, a, s in comp]
+        red = decompress_sum_compress(parts, block, target_energy)
+        shards.append(red)
+        out[sl] = decompress(*red, block)
+    return out, shards

@@ -430,3 +430,32 @@ def test_full_size_delayed(taco):
     bits = W.bf16_bits(W.make("gpt3_6p7b_act", seed=0))
     _, _, _, A = oracle.compress_delayed(bits, w.block, 1.0, 0.0)
     run_delayed(taco, bits, w.block, 1.0, float(np.float32(A)))
+
+
+# ------------------------------------------------------------ two-shot all-reduce emulation
+def run_two_shot(taco, xs_bits, block):
+    P = len(xs_bits)
+    T, H = xs_bits[0].shape
+    print(f"[case] two_shot_allreduce P={P} shape=({T},{H}) block={block}", flush=True)
+    got = W.bf16_bits(taco.two_shot_allreduce([to_gpu_bits(b) for b in xs_bits], block))
+    want, _ = oracle.two_shot_allreduce(xs_bits, block)
+    # two codec stages in sequence, each within 1e-3 of the oracle's
+    # reconstruction, so the chain within 2e-3
+    assert parity.rel_frobenius(got, want) <= 2e-3
+    exact = sum(oracle.bf16_bits_to_f64(b) for b in xs_bits)
+    err_g = np.linalg.norm(oracle.bf16_bits_to_f64(got) - exact) / np.linalg.norm(exact)
+    err_o = np.linalg.norm(oracle.bf16_bits_to_f64(want) - exact) / np.linalg.norm(exact)
+    print(f"[case]   error vs the exact sum: GPU {err_g:.5f} oracle {err_o:.5f}", flush=True)
+    assert abs(err_g - err_o) <= 0.05 * err_o + 1e-6
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8])
+def test_two_shot_allreduce_small(taco, engine, P):
+    xs = [W.bf16_bits(W.make("gpt3_6p7b_act", seed=20 + r, tokens=8 * P)) for r in range(P)]
+    run_two_shot(taco, xs, 128)
+
+
+def test_full_size_two_shot_allreduce(taco):
+    """4 ranks' [4096, 4096] activations at block 128: 1024-row shards."""
+    xs = [W.bf16_bits(W.make("gpt3_6p7b_act", seed=30 + r)) for r in range(4)]
+    run_two_shot(taco, xs, 128)

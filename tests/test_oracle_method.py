@@ -262,6 +262,27 @@ def test_decompress_sum_compress_is_the_composition_and_closed_forms():
     assert np.array_equal(q4, q) and np.allclose(a4, 2 * a, rtol=2 ** -22)
 
 
+def test_two_shot_allreduce_composition_and_error():
+    """The emulated two-shot all-reduce is its steps composed, and its result
+    stays close to the exact sum of the inputs."""
+    xs = [small_mix(8, 512, 40 + r) for r in range(4)]
+    out, shards = oracle.two_shot_allreduce(xs, 128)
+    comp = [oracle.compress(x, 128) for x in xs]
+    red = oracle.decompress_sum_compress([(q[2:4], a[2:4], s) for q, a, s in comp], 128)
+    for got, want in zip(shards[1], red):
+        assert np.array_equal(got, want)
+    assert np.array_equal(out[2:4], oracle.decompress(*red, 128))
+    exact = sum(f64_of(x) for x in xs)
+    assert np.linalg.norm(f64_of(out) - exact) <= 0.1 * np.linalg.norm(exact)
+    # one rank: compress, then compress the reconstruction again
+    one, _ = oracle.two_shot_allreduce(xs[:1], 128)
+    q, a, s = oracle.compress(xs[0], 128)
+    again = oracle.compress(oracle.decompress(q, a, s, 128), 128)
+    assert np.array_equal(one, oracle.decompress(*again, 128))
+    with pytest.raises(ValueError):
+        oracle.two_shot_allreduce([small_mix(6, 512, 1)] * 4, 128)
+
+
 def test_shape_and_argument_checks():
     x = np.zeros((2, 96), dtype=np.uint16)
     with pytest.raises(ValueError):
