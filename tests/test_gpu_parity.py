@@ -459,3 +459,80 @@ def test_full_size_two_shot_allreduce(taco):
     """4 ranks' [4096, 4096] activations at block 128: 1024-row shards."""
     xs = [W.bf16_bits(W.make("gpt3_6p7b_act", seed=30 + r)) for r in range(4)]
     run_two_shot(taco, xs, 128)
+
+
+# ------------------------------------------------------------ HIP graphs
+def test_graph_replays_match_eager(taco):
+    """Every entry point captured in one HIP graph (torch.cuda.CUDAGraph) and
+    replayed several times, with eager calls on the same workspaces between the
+    replays: every replay reproduces the eager results bitwise (the barrier
+    state carries over between calls by design)."""
+    T, H, B = 512, 4096, 128
+    dev = torch.device("cuda")
+    x1 = W.make("gpt3_6p7b_act", seed=11, tokens=T).to(dev)
+    x2 = W.make("gpt3_6p7b_grad", seed=12, tokens=T).to(dev)
+    ws = torch.zeros(taco.workspace_bytes(T, H, B), dtype=torch.uint8, device=dev)
+    ws2 = torch.zeros(taco.load().taco_decompress_sum_compress_workspace_bytes(T, H, B),
+                      dtype=torch.uint8, device=dev)
+    nb = T * H // B
+    out = {
+        "q1": torch.empty((T, H), dtype=torch.uint8, device=dev),
+        "a1": torch.empty((T, H // B), dtype=torch.float32, device=dev),
+        "s1": torch.empty(1, dtype=torch.float32, device=dev),
+        "q2": torch.empty((T, H), dtype=torch.uint8, device=dev),
+        "a2": torch.empty((T, H // B), dtype=torch.float32, device=dev),
+        "s2": torch.empty(1, dtype=torch.float32, device=dev),
+        "xh": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+        "sum": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+        "rq": torch.empty((T, H), dtype=torch.uint8, device=dev),
+        "ra": torch.empty((T, H // B), dtype=torch.float32, device=dev),
+        "rs": torch.empty(1, dtype=torch.float32, device=dev),
+        "bq": torch.empty((T, H), dtype=torch.uint8, device=dev),
+        "ba": torch.empty((T, H // B), dtype=torch.float32, device=dev),
+        "bs": torch.empty((T, H // B), dtype=torch.float32, device=dev),
+        "dq": torch.empty((T, H), dtype=torch.uint8, device=dev),
+        "da": torch.empty((T, H // B), dtype=torch.float32, device=dev),
+        "ds": torch.empty(1, dtype=torch.float32, device=dev),
+        "amax": torch.zeros(taco.TACO_AMAX_FLOATS, dtype=torch.float32, device=dev),
+        "prev": torch.zeros(taco.TACO_AMAX_FLOATS, dtype=torch.float32, device=dev),
+    }
+    out["prev"][0] = 3.0
+
+    def ops():
+        taco.compress(x1, B, q=out["q1"], alpha=out["a1"], scale=out["s1"], workspace=ws)
+        taco.compress(x2, B, q=out["q2"], alpha=out["a2"], scale=out["s2"], workspace=ws)
+        taco.decompress(out["q1"], out["a1"], out["s1"], B, out=out["xh"])
+        parts = [(out["q1"], out["a1"], out["s1"]), (out["q2"], out["a2"], out["s2"])]
+        taco.decompress_sum(parts, B, out=out["sum"])
+        taco.decompress_sum_compress(parts, B, q=out["rq"], alpha=out["ra"], scale=out["rs"], workspace=ws2)
+        taco.compress_blockscale(x2, B, 2.0 ** 12, q=out["bq"], alpha=out["ba"], scale=out["bs"])
+        out["amax"].zero_()
+        taco.compress_delayed(x1, B, out["prev"], q=out["dq"], alpha=out["da"], scale=out["ds"],
+                              amax_out=out["amax"])
+
+    ops()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in out.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ops()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops()
+    for rep in range(4):
+        for v in out.values():
+            if v.dtype == torch.uint8:
+                v.fill_(0x55)
+        g.replay()
+        torch.cuda.synchronize()
+        for k in eager:
+            assert torch.equal(out[k], eager[k]), (rep, k)
+        # eager work between the replays, on the same workspaces
+        taco.compress(x2, B, workspace=ws)
+        taco.decompress_sum_compress([(eager["q2"], eager["a2"], eager["s2"])], B, workspace=ws2)
+        torch.cuda.synchronize()
+    assert int(ws[8:12].cpu().numpy().view(np.uint32)[0]) == 0
+    assert int(ws2[8:12].cpu().numpy().view(np.uint32)[0]) == 0
