@@ -12,8 +12,10 @@ from ._binding import (  # noqa: F401
     compress,
     compress_blockscale,
     compress_delayed,
+    get_barrier_spin_limit,
     get_rotation_engine,
     get_single_pass,
+    set_barrier_spin_limit,
     set_rotation_engine,
     set_single_pass,
     two_shot_allreduce,
@@ -26,11 +28,12 @@ from ._binding import (  # noqa: F401
     num_scales,
     version,
     workspace_bytes,
+    workspace_timed_out,
 )
 
 __all__ = [
     "TACO_AMAX_FLOATS", "TACO_AMAX_SLOTS", "TACO_MAX_PARTS", "TacoError", "compress", "compress_blockscale",
-    "compress_delayed", "decompress", "decompress_blockscale", "decompress_sum", "decompress_sum_compress", "get_rotation_engine",
-    "get_single_pass", "library_path", "load", "num_scales", "set_rotation_engine", "set_single_pass", "two_shot_allreduce",
-    "version", "workspace_bytes",
+    "compress_delayed", "decompress", "decompress_blockscale", "decompress_sum", "decompress_sum_compress", "get_barrier_spin_limit", "get_rotation_engine",
+    "get_single_pass", "library_path", "load", "num_scales", "set_barrier_spin_limit", "set_rotation_engine", "set_single_pass", "two_shot_allreduce",
+    "version", "workspace_bytes", "workspace_timed_out",
 ]

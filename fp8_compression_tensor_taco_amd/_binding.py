@@ -71,6 +71,12 @@ def load() -> ctypes.CDLL:
         lib.taco_set_single_pass.argtypes = [ctypes.c_int]
         lib.taco_get_single_pass.restype = ctypes.c_int
         lib.taco_get_single_pass.argtypes = []
+        lib.taco_set_barrier_spin_limit.restype = None
+        lib.taco_set_barrier_spin_limit.argtypes = [ctypes.c_uint32]
+        lib.taco_get_barrier_spin_limit.restype = ctypes.c_uint32
+        lib.taco_get_barrier_spin_limit.argtypes = []
+        lib.taco_workspace_timed_out.restype = ctypes.c_int
+        lib.taco_workspace_timed_out.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_int)]
         lib.taco_num_scales.restype = _i64
         lib.taco_num_scales.argtypes = [_i64, _i64, _i32]
         lib.taco_compress_workspace_bytes.restype = ctypes.c_size_t
@@ -164,6 +170,34 @@ def set_single_pass(enable: bool) -> None:
 
 def get_single_pass() -> bool:
     return bool(load().taco_get_single_pass())
+
+
+def set_barrier_spin_limit(polls: int) -> None:
+    """Bound on the grid barrier's polls in the single-pass kernels (0: the
+    default, 2^22).  A workgroup that gives up stores NaN codes and sets the
+    workspace's timeout flag; every kernel still finishes."""
+    if not 0 <= int(polls) < 2 ** 32:
+        raise ValueError("polls must fit in 32 bits")
+    load().taco_set_barrier_spin_limit(int(polls))
+
+
+def get_barrier_spin_limit() -> int:
+    return int(load().taco_get_barrier_spin_limit())
+
+
+def workspace_timed_out(workspace: torch.Tensor | None = None, stream=None) -> bool:
+    """Whether a single-pass call on `workspace` has given up at its grid
+    barrier since the workspace was zero-filled (waits for the stream).  With
+    no argument, checks every workspace the binding has allocated."""
+    lib = load()
+    wss = [workspace] if workspace is not None else list(_workspaces.values())
+    for ws in wss:
+        dev = _require_gpu(ws)
+        flag = ctypes.c_int(0)
+        _check(lib.taco_workspace_timed_out(_ptr(ws), _stream(dev, stream), ctypes.byref(flag)))
+        if flag.value:
+            return True
+    return False
 
 
 def num_scales(tokens: int, hidden: int, block: int) -> int:

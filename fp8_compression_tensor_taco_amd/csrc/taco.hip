@@ -48,6 +48,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <cstddef>
 
 #include "taco.h"
 
@@ -497,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
     load_tile_mfma<B, false>(x, t < ntiles ? t : ntiles - 1, nblocks, xr[u]);
   }
   const float A = partials_max(partial, npartial, red);
-  const float s = A > 0.0f ? kQmax / A : 1.0f;
+  const float s = A == 0.0f ? 1.0f : kQmax / A;   // NaN stays NaN
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t t = t0 + u * nw;
@@ -543,15 +545,17 @@ __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
 // leaf's max with an atomic exchange against 0 (one lane per leaf; this also
 // clears them for the next call) and writes rel = (call + 1, max) into all
 // kLeaves leaf lines.  Everyone else polls its own leaf's rel.  The poll is
-// bounded: after kSpinLimit polls it records timed_out and goes on (the
-// result is then unspecified and the workspace must be zero-filled again, but
-// every wavefront finishes).
+// bounded (spin_limit polls, set by the host): a workgroup that gives up sets
+// the sticky timed_out flag and takes NaN as the max, so its codes are all
+// E4M3 NaN rather than plausible values under a stale scale.  It has already
+// arrived, so the barrier still completes for the others and the workspace
+// stays consistent for the next call; every wavefront finishes.
 
 constexpr int kLine = 256;               // bytes per barrier line
 constexpr int kLeafWgs = 16;             // workgroups per leaf
 constexpr int kLeaves = 64;              // leaf lines => at most 1024 fused workgroups
 constexpr size_t kPartialOffset = static_cast<size_t>(kLine) * (1 + kLeaves);
-constexpr unsigned kSpinLimit = 1u << 22;
+constexpr unsigned kDefaultSpinLimit = 1u << 22;
 
 struct RootLine {
   unsigned long long count;
@@ -585,8 +589,9 @@ __device__ __forceinline__ T add_agent(T* p, T v) {
 }
 
 // Grid-wide max; called by the 64 lanes of wavefront 0 with the workgroup's
-// max (uniform).  Every lane returns the tensor-wide max.
-__device__ float grid_max_wave0(float wg_max, char* __restrict__ ws) {
+// max (uniform).  Every lane returns the tensor-wide max, or NaN if this
+// workgroup gave up waiting.
+__device__ float grid_max_wave0(float wg_max, char* __restrict__ ws, unsigned spin_limit) {
   const int lane = threadIdx.x & 63;
   RootLine* root = reinterpret_cast<RootLine*>(ws);
   const unsigned l = blockIdx.x / kLeafWgs;
@@ -630,8 +635,9 @@ __device__ float grid_max_wave0(float wg_max, char* __restrict__ ws) {
   if (lane == 0) {
     unsigned spins = 0;
     while (((r = load_agent(&lf->rel)) >> 32) != (want >> 32)) {
-      if (++spins == kSpinLimit) {
+      if (++spins >= spin_limit) {
         store_agent(&root->timed_out, 1u);
+        r = 0x7FC00000u;   // quiet NaN: the codes of this workgroup become NaN
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -645,7 +651,7 @@ static_assert(kLeaves == 64, "grid_max_wave0 releases one leaf per lane");
 template <int B, int TPW, bool HOLD_Y, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
     const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
-    float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q) {
+    float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q, unsigned spin_limit) {
   constexpr int NK = B / 32, NM = B / 16, SROW = Blk<B>::kCodeRowMfma;
   __shared__ float red[WAVES];
   __shared__ float amax_sh;
@@ -687,12 +693,12 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
   }
   const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x < 64) {
-    const float A = grid_max_wave0(wg, ws);
+    const float A = grid_max_wave0(wg, ws, spin_limit);
     if (threadIdx.x == 0) amax_sh = A;
   }
   __syncthreads();
   const float A = amax_sh;
-  const float s = A > 0.0f ? kQmax / A : 1.0f;
+  const float s = A == 0.0f ? 1.0f : kQmax / A;   // NaN stays NaN
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
@@ -876,7 +882,7 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
 template <int B, int TPW, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     Parts parts, int nparts, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
-    float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q) {
+    float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q, unsigned spin_limit) {
   constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16, NK = B / 32, NM = B / 16;
   constexpr int XROW = 2 * B + 16, SROW = Blk<B>::kCodeRowMfma;
   constexpr int kLdsWave = kTileBlocks * (XROW > SROW ? XROW : SROW);
@@ -980,12 +986,12 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
   }
   const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x < 64) {
-    const float A = grid_max_wave0(wg, ws);
+    const float A = grid_max_wave0(wg, ws, spin_limit);
     if (threadIdx.x == 0) amax_sh = A;
   }
   __syncthreads();
   const float A = amax_sh;
-  const float s = A > 0.0f ? kQmax / A : 1.0f;
+  const float s = A == 0.0f ? 1.0f : kQmax / A;   // NaN stays NaN
   if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
@@ -1148,6 +1154,7 @@ int resident_grid(Kernel kernel, int threads) {
 taco_status_t launched() { return hipGetLastError() == hipSuccess ? TACO_OK : TACO_ERR_HIP; }
 
 int g_engine = TACO_ENGINE_AUTO;   // rotation engine of taco_compress (process-wide)
+std::atomic<unsigned> g_spin_limit{kDefaultSpinLimit};   // barrier poll bound (process-wide)
 
 // Launches the fused compress with TPW tiles per wavefront if every one of its
 // wavefronts can be resident at once (and the barrier has leaves for them).
@@ -1160,7 +1167,7 @@ bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, flo
   const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
   if (g > cap) return false;
   hipLaunchKernelGGL((compress_fused_kernel<B, TPW, HOLD_Y, WAVES>), dim3(g), dim3(64 * WAVES), 0,
-                     stream, x, nblocks, sqrt_eb, alpha, scale, ws, q);
+                     stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
   return true;
 }
 
@@ -1245,7 +1252,7 @@ bool try_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblocks
   const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
   if (g > cap) return false;
   hipLaunchKernelGGL((decompress_sum_compress_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
-                     stream, parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, q);
+                     stream, parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
   return true;
 }
 
@@ -1330,6 +1337,25 @@ taco_engine_t taco_get_rotation_engine(void) { return static_cast<taco_engine_t>
 void taco_set_single_pass(int enable) { g_single_pass = enable != 0; }
 
 int taco_get_single_pass(void) { return g_single_pass ? 1 : 0; }
+
+void taco_set_barrier_spin_limit(uint32_t polls) {
+  g_spin_limit.store(polls == 0 ? kDefaultSpinLimit : polls);
+}
+
+uint32_t taco_get_barrier_spin_limit(void) { return g_spin_limit.load(); }
+
+taco_status_t taco_workspace_timed_out(const void* workspace, void* stream, int* timed_out) {
+  if (workspace == nullptr || timed_out == nullptr) return TACO_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TACO_ERR_ALIGN;
+  unsigned flag = 0;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const char* root = static_cast<const char*>(workspace) + offsetof(RootLine, timed_out);
+  if (hipMemcpyAsync(&flag, root, sizeof(flag), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return TACO_ERR_HIP;
+  *timed_out = flag != 0 ? 1 : 0;
+  return TACO_OK;
+}
 
 int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block) {
   if (check_shape(tokens, hidden, block) != TACO_OK) return -1;

@@ -117,10 +117,30 @@ int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block);
  * the next one.  Calls that share a workspace must be ordered (the same
  * stream).  While a single-pass compress runs no other kernel may occupy the
  * GPU's compute units: its workgroups must all be resident at once to pass the
- * barrier; if they are not, the barrier gives up after a bounded wait and the
- * call's result is unspecified (taco_set_single_pass(0) removes the
- * requirement). */
+ * barrier; a workgroup that is not gives up after a bounded wait (see
+ * taco_set_barrier_spin_limit), and the codes of every workgroup that gave up
+ * are E4M3 NaN (0x7F / 0xFF), so the failure cannot pass for a result
+ * (taco_set_single_pass(0) removes the requirement).  A timeout also sets a
+ * sticky flag in the workspace (taco_workspace_timed_out); the workspace stays
+ * valid for later calls. */
 size_t taco_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block);
+
+/* Bound on the polls of the single-pass kernels' grid barrier, for the whole
+ * process (read when a call is made).  polls == 0 restores the default, 2^22
+ * polls (seconds; a barrier whose workgroups are all resident completes in
+ * microseconds).  A small bound makes waits give up early, e.g. to exercise
+ * the timeout path in tests: every kernel still finishes. */
+void taco_set_barrier_spin_limit(uint32_t polls);
+uint32_t taco_get_barrier_spin_limit(void);
+
+/* Whether a single-pass call on this workspace (of taco_compress or
+ * taco_decompress_sum_compress) has given up waiting at its grid barrier since
+ * the workspace was zero-filled: *timed_out = 1 if so, else 0.  Waits for the
+ * work queued on `stream` (a hipStream_t; NULL: the null stream) to finish, then
+ * reads 4 bytes of the workspace.  The flag is sticky: zero-fill the workspace
+ * to clear it.  TACO_ERR_NULL for a NULL pointer, TACO_ERR_ALIGN for a
+ * workspace not 256-byte aligned, TACO_ERR_HIP if the copy fails. */
+taco_status_t taco_workspace_timed_out(const void* workspace, void* stream, int* timed_out);
 
 /*
  * Compress: energy -> ASH scale -> Hadamard rotation -> DS scale -> FP8

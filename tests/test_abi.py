@@ -61,6 +61,23 @@ def test_host_only_queries(lib):
         assert lib.taco_set_rotation_engine(e) == 0 and lib.taco_get_rotation_engine() == e
 
 
+def test_barrier_spin_limit_setting(lib):
+    default = lib.taco_get_barrier_spin_limit()
+    assert default == 1 << 22
+    lib.taco_set_barrier_spin_limit(3)
+    assert lib.taco_get_barrier_spin_limit() == 3
+    lib.taco_set_barrier_spin_limit(0)                    # 0 restores the default
+    assert lib.taco_get_barrier_spin_limit() == default
+
+
+def test_workspace_timeout_query_checks_arguments(lib):
+    flag = ctypes.c_int(7)
+    assert lib.taco_workspace_timed_out(None, None, ctypes.byref(flag)) == 1
+    assert lib.taco_workspace_timed_out(ctypes.c_void_p(0x10000), None, None) == 1
+    assert lib.taco_workspace_timed_out(ctypes.c_void_p(0x10010), None, ctypes.byref(flag)) == 2
+    assert flag.value == 7                                # untouched on error
+
+
 FAKE = 0x10000        # 16-byte aligned, never dereferenced (every call below fails a check)
 
 

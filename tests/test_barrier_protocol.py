@@ -14,14 +14,19 @@ import random
 LEAF, LEAVES = 16, 64
 
 
-def run_calls(seed, calls):
+def run_calls(seed, calls, spin_limits=(None,)):
+    """spin_limits: per call, a bound on the polls is drawn from this list
+    (None: unbounded).  A workgroup that reaches the bound gives up (NaN, here
+    None) and sets timed_out; it has arrived, so the others still complete."""
     rnd = random.Random(seed)
+    timed_out = False
     leaf = [{"count": 0, "max": 0, "rel": 0} for _ in range(LEAVES)]
     root = {"count": 0}
     for _ in range(calls):
         G = rnd.choice([1, 2, 15, 16, 17, 100, 255, 256, 512, 1000, 1024])
         nleaves = (G + LEAF - 1) // LEAF
         vals = [rnd.randint(0, 10 ** 6) for _ in range(G)]
+        limit = rnd.choice(spin_limits)
 
         def workgroup(b):
             l = b // LEAF
@@ -58,6 +63,10 @@ def run_calls(seed, calls):
             while (leaf[l]["rel"] >> 32) != want:
                 spins += 1
                 assert spins < 10 ** 6, "endless wait"
+                if limit is not None and spins >= limit:
+                    nonlocal timed_out
+                    timed_out = True
+                    return None
                 yield
             return leaf[l]["rel"] & 0xFFFFFFFF
 
@@ -70,9 +79,23 @@ def run_calls(seed, calls):
             except StopIteration as e:
                 got[b] = e.value
                 del live[b]
-        assert all(v == max(vals) for v in got.values())
+        assert all(v is None or v == max(vals) for v in got.values())
+        assert sum(v is not None for v in got.values()) >= 1      # the completing workgroup
+        if limit is None:
+            assert all(v is not None for v in got.values())
+    return timed_out
 
 
 def test_barrier_protocol_random_interleavings():
     for seed in range(3):
-        run_calls(seed, 30)
+        assert not run_calls(seed, 30)
+
+
+def test_barrier_survives_workgroups_that_give_up():
+    """Calls whose waits are bounded (some workgroups give up) interleaved with
+    unbounded ones: the unbounded calls still all get the true maximum, so a
+    timeout leaves the barrier state consistent for the next call."""
+    gave_up = False
+    for seed in range(3, 6):
+        gave_up |= run_calls(seed, 30, spin_limits=(None, 1, 2, 8))
+    assert gave_up

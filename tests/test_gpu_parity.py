@@ -194,6 +194,69 @@ def test_fused_matches_two_pass_bitwise(taco):
         assert timed_out == 0
 
 
+def _tiles_equal_or_nan(q, ref, block):
+    """Per tile of 16 blocks: the codes equal the reference or are all NaN.
+    Returns (tiles equal, tiles NaN)."""
+    qt = q.reshape(-1, 16 * block)
+    rt = ref.reshape(-1, 16 * block)
+    eq = (qt == rt).all(dim=1)
+    nan = ((qt & 0x7F) == 0x7F).all(dim=1)
+    assert bool((eq | nan).all())
+    return int(eq.sum()), int(nan.sum())
+
+
+def test_barrier_timeout_gives_nan_codes_and_keeps_the_workspace(taco):
+    """The barrier's bounded wait, forced from the host with a bound of one
+    poll: the workgroups that give up store NaN codes (never plausible codes
+    under a stale scale), alpha is unaffected, the sticky flag is set, and the
+    workspace stays valid for the next call."""
+    block = 128
+    x = W.make("gpt3_6p7b_act", seed=4096, tokens=4096).cuda()
+    ref = _compress_with(taco, x, block, False, torch.zeros(taco.workspace_bytes(4096, 4096, block),
+                                                             dtype=torch.uint8, device="cuda"))
+    ws = torch.zeros(taco.workspace_bytes(4096, 4096, block), dtype=torch.uint8, device="cuda")
+    print("[case] fused compress, barrier bound of 1 poll", flush=True)
+    taco.set_barrier_spin_limit(1)
+    try:
+        q, a, s = _compress_with(taco, x, block, True, ws)
+    finally:
+        taco.set_barrier_spin_limit(0)
+    assert taco.workspace_timed_out(ws)
+    eq, nan = _tiles_equal_or_nan(q, ref[0], block)
+    assert eq >= 1 and nan >= 1
+    assert torch.equal(a, ref[1])
+    assert torch.equal(s, ref[2]) or bool(torch.isnan(s).all())
+    print("[case] fused compress after the timeout, same workspace", flush=True)
+    for r, t in zip(ref, _compress_with(taco, x, block, True, ws)):
+        assert torch.equal(r, t)
+    assert taco.workspace_timed_out(ws)                 # sticky until zero-filled
+    ws.zero_()
+    assert not taco.workspace_timed_out(ws)
+    for r, t in zip(ref, _compress_with(taco, x, block, True, ws)):
+        assert torch.equal(r, t)
+    assert not taco.workspace_timed_out(ws)
+
+    print("[case] fused decompress-sum-compress, barrier bound of 1 poll", flush=True)
+    parts = [taco.compress(W.make("gpt3_6p7b_act", seed=40 + i, tokens=4096).cuda(), block)
+             for i in range(2)]
+    parts = [tuple(t.clone() for t in p) for p in parts]
+    ws2 = torch.zeros(taco.load().taco_decompress_sum_compress_workspace_bytes(4096, 4096, block),
+                      dtype=torch.uint8, device="cuda")
+    ref2 = [t.clone() for t in taco.decompress_sum_compress(parts, block, workspace=ws2)]
+    assert not taco.workspace_timed_out(ws2)
+    taco.set_barrier_spin_limit(1)
+    try:
+        q2, a2, s2 = [t.clone() for t in taco.decompress_sum_compress(parts, block, workspace=ws2)]
+    finally:
+        taco.set_barrier_spin_limit(0)
+    assert taco.workspace_timed_out(ws2)
+    eq, nan = _tiles_equal_or_nan(q2, ref2[0], block)
+    assert eq >= 1 and nan >= 1
+    assert torch.equal(a2, ref2[1])
+    for r, t in zip(ref2, taco.decompress_sum_compress(parts, block, workspace=ws2)):
+        assert torch.equal(r, t)
+
+
 def test_determinism(taco, engine):
     x = W.make("gpt2_1p5b", seed=3, tokens=512).cuda()
     r1 = [t.clone() for t in taco.compress(x, 64)]
