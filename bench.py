@@ -14,10 +14,14 @@ HBM rather than the 256 MB Infinity Cache, the step rotates over R complete
 buffer sets (>= 1 GiB together).  `value` is bf16 bytes moved by the calls
 (bf16 in for compress, bf16 out for the decompressions) per second.
 
-Each step is launched as one HIP graph (captured per buffer set), so the timed
-region measures the GPU rather than the host's per-call enqueue cost.  The
-per-op durations (and the roofline of the compress kernels) come from their own
-timed regions: graphs of back-to-back calls of one op over every buffer set.
+Steps are launched as HIP graphs, so the timed region measures the GPU rather
+than the host's per-call enqueue cost: one graph holds one step per buffer set
+(R steps, replayed K // R times; any remaining steps replay single-step
+graphs), because consecutive graph launches leave a gap of several
+microseconds on the GPU that one launch per step would add to every step.
+Every step still does all of its work.  The per-op durations (and the roofline
+of the compress kernels) come from their own timed regions: graphs of
+back-to-back calls of one op, OP_PASSES passes over every buffer set.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -38,6 +42,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 WORKLOAD = "gpt3_6p7b"
 TOKENS, HIDDEN, BLOCK, NPARTS = 4096, 4096, 128, 4
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "compress_gpt3_6p7b_counters.json")
+OP_PASSES = 4                    # passes over the buffer sets per per-op graph
 
 
 def parse():
@@ -219,18 +224,24 @@ def main():
         return g
 
     step_graphs = [capture(lambda st=st: step(st)) for st in sets]
+    cycle_graph = capture(lambda: [step(st) for st in sets])
+    P = OP_PASSES
     op_graphs = {
-        "compress": (capture(lambda: [op_compress(st, k) for st in sets for k in range(2)]), 2 * len(sets)),
-        "decompress": (capture(lambda: [op_decompress(st, k) for st in sets for k in range(2)]), 2 * len(sets)),
-        "decompress_sum": (capture(lambda: [op_sum(st) for st in sets]), len(sets)),
-        "decompress_sum_compress": (capture(lambda: [op_sum_compress(st) for st in sets]), len(sets)),
-        "compress_blockscale": (capture(lambda: [op_blockscale(st, k) for st in sets for k in range(2)]),
-                                2 * len(sets)),
-        "decompress_blockscale": (capture(lambda: [op_blockscale_dec(st, k) for st in sets for k in range(2)]),
-                                  2 * len(sets)),
-        "compress_delayed": (capture(lambda: [op_delayed(st, k) for st in sets for k in range(2)]),
-                             2 * len(sets)),
+        "compress": (capture(lambda: [op_compress(st, k) for _ in range(P) for st in sets for k in range(2)]),
+                     2 * P * len(sets)),
+        "decompress": (capture(lambda: [op_decompress(st, k) for _ in range(P) for st in sets for k in range(2)]),
+                       2 * P * len(sets)),
+        "decompress_sum": (capture(lambda: [op_sum(st) for _ in range(P) for st in sets]), P * len(sets)),
+        "decompress_sum_compress": (capture(lambda: [op_sum_compress(st) for _ in range(P) for st in sets]),
+                                    P * len(sets)),
+        "compress_blockscale": (capture(lambda: [op_blockscale(st, k) for _ in range(P) for st in sets
+                                                 for k in range(2)]), 2 * P * len(sets)),
+        "decompress_blockscale": (capture(lambda: [op_blockscale_dec(st, k) for _ in range(P) for st in sets
+                                                   for k in range(2)]), 2 * P * len(sets)),
+        "compress_delayed": (capture(lambda: [op_delayed(st, k) for _ in range(P) for st in sets
+                                              for k in range(2)]), 2 * P * len(sets)),
     }
+    cycle_graph.replay()
     for g in step_graphs:
         g.replay()
     for g, _ in op_graphs.values():
@@ -243,15 +254,18 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
-        step_graphs[i % len(step_graphs)].replay()
+    cycles, rest = divmod(args.steps, len(sets))
+    for _ in range(cycles):
+        cycle_graph.replay()                     # steps on sets 0 .. R-1
+    for i in range(rest):
+        step_graphs[i].replay()
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms_step = start.elapsed_time(end) / args.steps
 
     # ---- per-op timed regions: average duration of one call of each op
-    reps = max(1, args.steps // 4)
+    reps = max(1, args.steps // (4 * OP_PASSES))
     avg_us = {}
     extra = ["decompress_sum_compress", "compress_blockscale", "decompress_blockscale", "compress_delayed"]
     for op in ops + extra:
@@ -331,8 +345,8 @@ def main():
         "extra_ops_note": "not part of the step: decompress_sum_compress (4 parts -> FP8 of their bf16 "
                           "sum), the per-block-guard and delayed-scale Dual-Scale variants",
         "wall_s_timed": round(t_wall, 4),
-        "timing": "step = one HIP-graph replay of the 5 calls; per-op figures from graphs of back-to-back "
-                  "calls over all buffer sets",
+        "timing": "steps replayed as HIP graphs of one step per buffer set (each step all 5 calls); per-op "
+                  f"figures from graphs of back-to-back calls, {OP_PASSES} passes over all buffer sets",
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows, args.cpu_seconds)

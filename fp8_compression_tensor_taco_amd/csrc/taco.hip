@@ -88,7 +88,8 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // Streaming accesses.  Non-temporal stores of the outputs leave no dirty
 // lines in L2 for the end-of-kernel write-back (measured: compress 17.2 ->
 // 15.0 us, decompress 13.7 -> 12.1 us per call on [4096, 4096]; the
-// decompress-sum output measured no better, so it keeps ordinary stores).
+// decompress-sum output gains only together with its 16-byte code loads:
+// 22.5 -> 20.1 us for 4 parts).
 // x is read non-temporally by the fused kernel (14.9 -> 14.2 us), but not by
 // the two-pass kernels (the quantisation pass reads the statistics pass's
 // data again from the cache; non-temporal loads there measured slower).
@@ -103,7 +104,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #define TACO_NT_OUT_STORES 1
 #endif
 #ifndef TACO_NT_SUM_STORES
-#define TACO_NT_SUM_STORES 0
+#define TACO_NT_SUM_STORES 1
 #endif
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
@@ -214,6 +215,31 @@ __device__ __forceinline__ void fwht_across_quad(float (&v)[NA][8], float c1, fl
   for (int a = 0; a < NA; ++a)
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[a][j] = fmaf(dpp<kQuadXor2>(v[a][j]), c2, v[a][j]);
+}
+
+// One butterfly stage on an index bit held across the quad (CTRL: the DPP
+// quad permutation that pairs the lanes differing in it), with its sign debt c.
+template <int NA, int CTRL>
+__device__ __forceinline__ void fwht_quad_stage(float (&v)[NA][8], float c) {
+#pragma unroll
+  for (int a = 0; a < NA; ++a)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[a][j] = fmaf(dpp<CTRL>(v[a][j]), c, v[a][j]);
+}
+
+// One butterfly stage on the index bit that selects chunk c or c + H.
+template <int NA, int H>
+__device__ __forceinline__ void fwht_chunk_stage(float (&v)[NA][8]) {
+#pragma unroll
+  for (int a = 0; a < NA; a += 2 * H)
+#pragma unroll
+    for (int c = a; c < a + H; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = v[c][j], y = v[c + H][j];
+        v[c][j] = x + y;
+        v[c + H][j] = x - y;
+      }
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -729,6 +755,55 @@ __device__ __forceinline__ void rotate_f32(float (&v)[NA][8], const Quad& qd) {
   fwht_across_quad<NA>(v, qd.c1, qd.c2);
 }
 
+// The wide layout, used where 16-byte code loads pay (the sums of parts):
+// within each 64-element group g of a block, quad lane ql holds the 16
+// consecutive elements 64 g + 16 ql + (0..15), as chunks 2 g (first 8) and
+// 2 g + 1, so one 16-byte load moves a lane's codes.  Index bits 0-2 lie in a
+// chunk, bit 3 selects the chunk of the pair, bits 4-5 the quad lane and bits
+// 6.. the group.  The butterflies run over the index bits in the order
+// rotate_f32 uses in the quad layout (0-2, 5, 6.., 3, 4), so every value has
+// the magnitude it has there; only the sign of an exact zero can differ,
+// because the sign debt falls on other lanes.
+template <int NA>
+__device__ __forceinline__ void rotate_wide(float (&v)[NA][8], const Quad& qd) {
+#pragma unroll
+  for (int a = 0; a < NA; ++a) fwht_chunk<1>(v[a]);
+  fwht_quad_stage<NA, kQuadXor2>(v, qd.c2);           // bit 5
+  if constexpr (NA >= 4) fwht_chunk_stage<NA, 2>(v);  // bit 6
+  if constexpr (NA >= 8) fwht_chunk_stage<NA, 4>(v);  // bit 7
+  fwht_chunk_stage<NA, 1>(v);                         // bit 3
+  fwht_quad_stage<NA, kQuadXor1>(v, qd.c1);           // bit 4
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint4 dpp_u32x4(uint4 v) {
+  return make_uint4(__builtin_amdgcn_mov_dpp(static_cast<int>(v.x), CTRL, 0xF, 0xF, true),
+                    __builtin_amdgcn_mov_dpp(static_cast<int>(v.y), CTRL, 0xF, 0xF, true),
+                    __builtin_amdgcn_mov_dpp(static_cast<int>(v.z), CTRL, 0xF, 0xF, true),
+                    __builtin_amdgcn_mov_dpp(static_cast<int>(v.w), CTRL, 0xF, 0xF, true));
+}
+
+// Stores one block's bf16 values (times c) from the wide layout: the 16-byte
+// pieces are exchanged across the quad first, so that each store instruction
+// writes 64 contiguous bytes per quad (lane ql writes piece ql, then piece
+// 4 + ql, of each 128-byte group; piece i belongs to lane i / 2).
+template <int NA, bool NT>
+__device__ __forceinline__ void store_wide_bf16(uint4* __restrict__ blk_out, const float (&v)[NA][8],
+                                                float c, int ql, bool ok) {
+  constexpr int kLow = 0x50, kHigh = 0xFA;   // DPP quad_perm [0,0,1,1] and [2,2,3,3]
+  const bool odd = ql & 1;
+#pragma unroll
+  for (int g = 0; g < NA / 2; ++g) {
+    const uint4 p0 = to_bf16x8(v[2 * g], c), p1 = to_bf16x8(v[2 * g + 1], c);
+    const uint4 l0 = dpp_u32x4<kLow>(p0), l1 = dpp_u32x4<kLow>(p1);
+    const uint4 h0 = dpp_u32x4<kHigh>(p0), h1 = dpp_u32x4<kHigh>(p1);
+    if (ok) {
+      store16<NT>(&blk_out[8 * g + ql], odd ? l1 : l0);
+      store16<NT>(&blk_out[8 * g + 4 + ql], odd ? h1 : h0);
+    }
+  }
+}
+
 // Decompress: decode, rotate, multiply by 1/(alpha_k s sqrt(B)), round to
 // bf16.  Global accesses are direct, in the quad layout: one load instruction
 // moves 32 contiguous bytes of codes per quad, one store 64 contiguous bytes
@@ -802,13 +877,39 @@ __device__ __forceinline__ T pick(const T (&arr)[TACO_MAX_PARTS], int i) {
   return r;
 }
 
+// One block's codes in the wide layout (a block is 2 NA 16-byte pieces), one
+// 16-byte load per 64-element group, kept as 8-code chunks (zero when !ok).
+template <int NA>
+__device__ __forceinline__ void load_codes_wide(const uint4* __restrict__ q, int64_t k, int ql, bool ok,
+                                                uint2 (&c)[NA]) {
+#pragma unroll
+  for (int g = 0; g < NA / 2; ++g) {
+    const uint4 v = ok ? load16<TACO_NT_Q_LOADS != 0>(&q[k * (2 * NA) + 4 * g + ql]) : make_uint4(0, 0, 0, 0);
+    c[2 * g] = make_uint2(v.x, v.y);
+    c[2 * g + 1] = make_uint2(v.z, v.w);
+  }
+}
+
+// acc += decode(codes) * w, chunk by chunk.
+template <int NA>
+__device__ __forceinline__ void accumulate_chunks(float (&acc)[NA][8], const uint2 (&c)[NA], float w) {
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    float d[8];
+    from_fp8x8(c[a], d);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[a][j] = add_product(acc[a][j], d[j], w);
+  }
+}
+
 // Decompress-and-sum.  The rotation is linear, so the parts are combined
 // before it: acc = sum_p decode(q_p) / (alpha_{p,k} s_p), then one rotation
 // and the 1/sqrt(B) factor.  This is the same sum as decompressing each part
-// and adding the results, with P-1 fewer transforms per block.  Global
-// accesses as in decompress_kernel; the codes of all P parts of U tiles are
-// loaded before any is used.
-template <int B, int P, int U>
+// and adding the results, with P-1 fewer transforms per block.  Wide layout:
+// each lane loads its 16 codes of every 64-element group with one 16-byte
+// load per part, all parts' loads issued before any is used, and the bf16
+// result leaves through store_wide_bf16.
+template <int B, int P>
 __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
     Parts parts, int64_t nblocks, uint4* __restrict__ out) {
   constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16;
@@ -818,51 +919,25 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
   for (int p = 0; p < P; ++p) s[p] = *parts.scale[p];
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
-       t0 += W * U) {
-    uint2 raw[U][P][NA];
-    float wt[U][P];
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t < ntiles; t += W) {
+    const int64_t k = t * kTileBlocks + qd.blk;
+    const bool ok = k < nblocks;
+    uint2 raw[P][NA];
+    float wt[P];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kTileBlocks + qd.blk;
-      const bool ok = t0 + u * W < ntiles && k < nblocks;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const uint2* qp = reinterpret_cast<const uint2*>(parts.q[p]);
-#pragma unroll
-        for (int a = 0; a < NA; ++a)
-          raw[u][p][a] = ok ? load8<TACO_NT_Q_LOADS != 0>(&qp[k * C16 + 4 * a + qd.ql]) : make_uint2(0, 0);
-        wt[u][p] = ok ? parts.alpha[p][k] : 1.0f;
-      }
+    for (int p = 0; p < P; ++p) {
+      load_codes_wide<NA>(parts.q[p], k, qd.ql, ok, raw[p]);
+      wt[p] = ok ? parts.alpha[p][k] : 1.0f;
     }
+    float acc[NA][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kTileBlocks + qd.blk;
-      const bool ok = t0 + u * W < ntiles && k < nblocks;
-      float acc[NA][8];
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-      for (int a = 0; a < NA; ++a)
+      for (int j = 0; j < 8; ++j) acc[a][j] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[a][j] = 0.0f;
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        const float wp = 1.0f / (wt[u][p] * s[p]);
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-          float d[8];
-          from_fp8x8(raw[u][p][a], d);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) acc[a][j] = add_product(acc[a][j], d[j], wp);
-        }
-      }
-      rotate_f32<NA>(acc, qd);
-      const float r = Blk<B>::rsqrt_b * qd.debt;
-#pragma unroll
-      for (int a = 0; a < NA; ++a) {
-        const uint4 o = to_bf16x8(acc[a], r);
-        if (ok) store16<TACO_NT_SUM_STORES != 0>(&out[k * C16 + 4 * a + qd.ql], o);
-      }
-    }
+    for (int p = 0; p < P; ++p) accumulate_chunks<NA>(acc, raw[p], 1.0f / (wt[p] * s[p]));
+    rotate_wide<NA>(acc, qd);
+    store_wide_bf16<NA, TACO_NT_SUM_STORES != 0>(out + k * C16, acc, Blk<B>::rsqrt_b * qd.debt, qd.ql, ok);
   }
 }
 
@@ -883,7 +958,7 @@ template <int B, int TPW, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     Parts parts, int nparts, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
     float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q, unsigned spin_limit) {
-  constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16, NK = B / 32, NM = B / 16;
+  constexpr int NA = Blk<B>::NA, NK = B / 32, NM = B / 16;
   constexpr int XROW = 2 * B + 16, SROW = Blk<B>::kCodeRowMfma;
   constexpr int kLdsWave = kTileBlocks * (XROW > SROW ? XROW : SROW);
   __shared__ float red[WAVES];
@@ -903,7 +978,7 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     const int64_t t = wid + i * nw;
     const int64_t tc = t < ntiles ? t : ntiles - 1;
     const int rv = rows_valid(tc, nblocks);
-    // this lane's block in the quad layout (rows past the end read the last block)
+    // this lane's block in the wide layout (rows past the end read the last block)
     const int64_t kq = tc * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1);
     float acc[NA][8];
 #pragma unroll
@@ -912,20 +987,16 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
       for (int j = 0; j < 8; ++j) acc[a][j] = 0.0f;
     uint2 cur[NA], nxt[NA];
     float wcur, wnxt, scur, snxt;
-    {
-      const uint2* q0 = reinterpret_cast<const uint2*>(parts.q[0]);
-#pragma unroll
-      for (int a = 0; a < NA; ++a) cur[a] = q0[kq * C16 + 4 * a + qd.ql];
-      wcur = parts.alpha[0][kq];
-      scur = *parts.scale[0];
-    }
+    load_codes_wide<NA>(parts.q[0], kq, qd.ql, true, cur);
+    wcur = parts.alpha[0][kq];
+    scur = *parts.scale[0];
     for (int p = 0; p < nparts; ++p) {
       const int pn = p + 1 < nparts ? p + 1 : p;        // the last trip reloads itself
-      const uint2* qn = reinterpret_cast<const uint2*>(pick(parts.q, pn));
-#pragma unroll
-      for (int a = 0; a < NA; ++a) nxt[a] = qn[kq * C16 + 4 * a + qd.ql];
+      load_codes_wide<NA>(pick(parts.q, pn), kq, qd.ql, true, nxt);
       wnxt = pick(parts.alpha, pn)[kq];
       snxt = *pick(parts.scale, pn);
+      // (written out here rather than through accumulate_chunks: the call
+      // form made the allocator spill at B = 128, TPW = 2)
       const float wp = 1.0f / (wcur * scur);
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
@@ -939,11 +1010,13 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
       wcur = wnxt;
       scur = snxt;
     }
-    rotate_f32<NA>(acc, qd);
+    rotate_wide<NA>(acc, qd);
     const float r = Blk<B>::rsqrt_b * qd.debt;
+    // chunk 2 g2 + h holds elements 64 g2 + 16 ql + 8 h + (0..7)
 #pragma unroll
     for (int a = 0; a < NA; ++a)
-      *reinterpret_cast<uint4*>(lds + qd.blk * XROW + 64 * a + 16 * qd.ql) = to_bf16x8(acc[a], r);
+      *reinterpret_cast<uint4*>(lds + qd.blk * XROW + 128 * (a >> 1) + 32 * qd.ql + 16 * (a & 1)) =
+          to_bf16x8(acc[a], r);
     __builtin_amdgcn_wave_barrier();
     // The MFMA operand is read from LDS one K-step at a time (few live
     // registers); every sum is accumulated in the same order as
@@ -1219,7 +1292,7 @@ void launch_decompress(const uint8_t* q, const float* alpha, const float* scale,
 
 template <int B, int P>
 void launch_decompress_sum_p(const Parts& parts, int64_t nblocks, void* out, hipStream_t stream) {
-  hipLaunchKernelGGL((decompress_sum_kernel<B, P, 1>), dim3(tile_grid(nblocks)), dim3(kThreads), 0,
+  hipLaunchKernelGGL((decompress_sum_kernel<B, P>), dim3(tile_grid(nblocks)), dim3(kThreads), 0,
                      stream, parts, nblocks, static_cast<uint4*>(out));
 }
 
