@@ -11,7 +11,8 @@ once before timing, as the peers would do on their own GPUs).
 
 Inputs are resident in HBM when timing starts.  To keep the timed traffic in
 HBM rather than the 256 MB Infinity Cache, the step rotates over R complete
-buffer sets (>= 1 GiB together).  `value` is bf16 bytes moved by the calls
+buffer sets (16 by default, 4.3 GB together: even the op with the smallest
+inputs, decompress, reads 2 x 16 x 16.8 MB per rotation, twice the cache).  `value` is bf16 bytes moved by the calls
 (bf16 in for compress, bf16 out for the decompressions) per second.
 
 Steps are launched as HIP graphs, so the timed region measures the GPU rather
@@ -42,7 +43,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 WORKLOAD = "gpt3_6p7b"
 TOKENS, HIDDEN, BLOCK, NPARTS = 4096, 4096, 128, 4
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "compress_gpt3_6p7b_counters.json")
-OP_PASSES = 4                    # passes over the buffer sets per per-op graph
+OP_PASSES = 2                    # passes over the buffer sets per per-op graph
 
 
 def parse():
@@ -50,7 +51,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--rotate", type=int, default=4, help="buffer sets rotated over (>= 1 GiB total)")
+    p.add_argument("--rotate", type=int, default=16,
+                   help="buffer sets rotated over (16: 4.3 GB, so that every op's inputs over one "
+                        "rotation exceed the 256 MB Infinity Cache at least twice)")
     p.add_argument("--cpu-rows", type=int, default=TOKENS,
                    help="rows of the workload the oracle is timed on (cpu_baseline)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
