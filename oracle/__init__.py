@@ -3,6 +3,13 @@
 Test infrastructure only: see ``oracle/taco_oracle.py`` for what it computes and
 which passages it follows.  Product code never imports this package.
 """
+from .int8 import (  # noqa: F401
+    compress_int8_block,
+    compress_int8_tensor,
+    decompress_int8,
+    decompress_int8_f64,
+    int8_scale,
+)
 from .taco_oracle import (  # noqa: F401
     Q_MAX,
     ash_scale,

@@ -16,8 +16,9 @@ Gaussian-like], measured on tensors directly instead of through training:
   fp8_ash        ASH only (no rotation), per-tensor scale
   taco           ASH + rotation + per-tensor scale (oracle.compress)
 
-Readings: INT8 rounds to nearest even and clips at +-127 (the pages give no
-INT8 details); each FP8 ablation keeps the rest of the method unchanged.
+Readings: the INT8 rows are oracle/int8.py's quantiser (round half to even,
+clip at +-127, decisions in fp32; the pages give no INT8 details); each FP8
+ablation keeps the rest of the method unchanged.
 Every function returns the fp64 reconstruction (before any bf16 rounding) and
 the values handed to the rounding step, so that collapse can be measured in
 the code domain.
@@ -26,14 +27,10 @@ from __future__ import annotations
 
 import numpy as np
 
+from . import int8 as i8
 from . import taco_oracle as o
 
 METHODS = ("int8_tensor", "int8_block", "fp8_plain", "fp8_hadamard", "fp8_ash", "taco")
-
-
-def _int8(v: np.ndarray, scale) -> tuple[np.ndarray, np.ndarray]:
-    q = np.clip(np.rint(v * scale), -127, 127)
-    return q / scale, v * scale
 
 
 def _fp8(v: np.ndarray, s) -> tuple[np.ndarray, np.ndarray]:
@@ -52,11 +49,13 @@ def quantise(method: str, x_bits: np.ndarray, block: int, target_energy: float =
     T, H = x.shape
     xb = x.reshape(-1, block)
     if method == "int8_tensor":
-        r, v = _int8(xb, np.float64(_tensor_scale(xb, 127.0)))
+        q, sc = i8.compress_int8_tensor(x_bits)
+        r = i8.decompress_int8_f64(q, sc, 0)
+        v = (x.astype(np.float32) * sc).astype(np.float64)
     elif method == "int8_block":
-        m = np.max(np.abs(xb), axis=1, keepdims=True)
-        sc = np.where(m > 0, (127.0 / np.where(m > 0, m, 1.0)).astype(np.float32), np.float32(1.0))
-        r, v = _int8(xb, sc.astype(np.float64))
+        q, sc = i8.compress_int8_block(x_bits, block)
+        r = i8.decompress_int8_f64(q, sc, block)
+        v = (x.astype(np.float32) * np.repeat(sc, block, axis=1)).astype(np.float64)
     elif method == "fp8_plain":
         r, v = _fp8(xb, _tensor_scale(xb, o.Q_MAX))
     elif method == "fp8_hadamard":
