@@ -204,6 +204,15 @@ def main():
         taco.compress_delayed(x, BLOCK, amax[0], q=st["q"][k], alpha=st["a"][k], scale=st["s"][k],
                               amax_out=amax[1])
 
+    def op_int8(st, k, block):
+        x = st["act"] if k == 0 else st["grad"]
+        taco.compress_int8(x, block, q=st["q"][k].view(torch.int8),
+                           scale=st["s"][k] if block == 0 else st["sblk"], workspace=ws)
+
+    def op_int8_dec(st, k, block):
+        taco.decompress_int8(st["q"][k].view(torch.int8), st["s"][k] if block == 0 else st["sblk"], block,
+                             out=st["xh"][k])
+
     def op_sum_compress(st):
         taco.decompress_sum_compress(st["parts"], BLOCK, q=st["rq"], alpha=st["ra"], scale=st["rs"],
                                      workspace=ws_rs)
@@ -243,6 +252,14 @@ def main():
                                                    for k in range(2)]), 2 * P * len(sets)),
         "compress_delayed": (capture(lambda: [op_delayed(st, k) for _ in range(P) for st in sets
                                               for k in range(2)]), 2 * P * len(sets)),
+        "compress_int8_tensor": (capture(lambda: [op_int8(st, k, 0) for _ in range(P) for st in sets
+                                                  for k in range(2)]), 2 * P * len(sets)),
+        "decompress_int8_tensor": (capture(lambda: [op_int8_dec(st, k, 0) for _ in range(P) for st in sets
+                                                    for k in range(2)]), 2 * P * len(sets)),
+        "compress_int8_block": (capture(lambda: [op_int8(st, k, BLOCK) for _ in range(P) for st in sets
+                                                 for k in range(2)]), 2 * P * len(sets)),
+        "decompress_int8_block": (capture(lambda: [op_int8_dec(st, k, BLOCK) for _ in range(P) for st in sets
+                                                   for k in range(2)]), 2 * P * len(sets)),
     }
     cycle_graph.replay()
     for g in step_graphs:
@@ -270,7 +287,8 @@ def main():
     # ---- per-op timed regions: average duration of one call of each op
     reps = max(1, args.steps // (4 * OP_PASSES))
     avg_us = {}
-    extra = ["decompress_sum_compress", "compress_blockscale", "decompress_blockscale", "compress_delayed"]
+    extra = ["decompress_sum_compress", "compress_blockscale", "decompress_blockscale", "compress_delayed",
+             "compress_int8_tensor", "decompress_int8_tensor", "compress_int8_block", "decompress_int8_block"]
     for op in ops + extra:
         g, calls = op_graphs[op]
         e0 = torch.cuda.Event(enable_timing=True)
@@ -294,6 +312,10 @@ def main():
         "compress_blockscale": 3 * N + 8 * nscales,
         "decompress_blockscale": 3 * N + 8 * nscales,
         "compress_delayed": 3 * N + 4 * nscales + 4,
+        "compress_int8_tensor": 3 * N + 4,
+        "decompress_int8_tensor": 3 * N + 4,
+        "compress_int8_block": 3 * N + 4 * nscales,
+        "decompress_int8_block": 3 * N + 4 * nscales,
     }
     achieved = alg["compress"] / (avg_us["compress"] * 1e-6) / 1e9
     traffic = measured_traffic()
@@ -346,7 +368,8 @@ def main():
             for op in extra
         },
         "extra_ops_note": "not part of the step: decompress_sum_compress (4 parts -> FP8 of their bf16 "
-                          "sum), the per-block-guard and delayed-scale Dual-Scale variants",
+                          "sum), the per-block-guard and delayed-scale Dual-Scale variants, and the INT8 "
+                          "degrade path (absmax per tensor: two kernels, x read twice; per 128-block)",
         "wall_s_timed": round(t_wall, 4),
         "timing": "steps replayed as HIP graphs of one step per buffer set (each step all 5 calls); per-op "
                   f"figures from graphs of back-to-back calls, {OP_PASSES} passes over all buffer sets",

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     compress,
     compress_blockscale,
     compress_delayed,
+    compress_int8,
     get_barrier_spin_limit,
     get_rotation_engine,
     get_single_pass,
@@ -21,6 +22,7 @@ from ._binding import (  # noqa: F401
     two_shot_allreduce,
     decompress,
     decompress_blockscale,
+    decompress_int8,
     decompress_sum,
     decompress_sum_compress,
     library_path,
@@ -33,7 +35,7 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "TACO_AMAX_FLOATS", "TACO_AMAX_SLOTS", "TACO_MAX_PARTS", "TacoError", "compress", "compress_blockscale",
-    "compress_delayed", "decompress", "decompress_blockscale", "decompress_sum", "decompress_sum_compress", "get_barrier_spin_limit", "get_rotation_engine",
+    "compress_delayed", "compress_int8", "decompress", "decompress_blockscale", "decompress_int8", "decompress_sum", "decompress_sum_compress", "get_barrier_spin_limit", "get_rotation_engine",
     "get_single_pass", "library_path", "load", "num_scales", "set_barrier_spin_limit", "set_rotation_engine", "set_single_pass", "two_shot_allreduce",
     "version", "workspace_bytes", "workspace_timed_out",
 ]

@@ -100,6 +100,12 @@ def load() -> ctypes.CDLL:
         lib.taco_compress_delayed.restype = ctypes.c_int
         lib.taco_compress_delayed.argtypes = [_vp, _i64, _i64, _i32, ctypes.c_float, _vp, _vp, _vp, _vp,
                                               _vp, _vp]
+        lib.taco_compress_int8_workspace_bytes.restype = ctypes.c_size_t
+        lib.taco_compress_int8_workspace_bytes.argtypes = [_i64, _i64, _i32]
+        lib.taco_compress_int8.restype = ctypes.c_int
+        lib.taco_compress_int8.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+        lib.taco_decompress_int8.restype = ctypes.c_int
+        lib.taco_decompress_int8.argtypes = [_vp, _vp, _i64, _i64, _i32, _vp, _vp]
         lib.taco_decompress_sum.restype = ctypes.c_int
         lib.taco_decompress_sum.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                             ctypes.POINTER(_vp), _i32, _i64, _i64, _i32, _vp, _vp]
@@ -423,6 +429,69 @@ def decompress_blockscale(q: torch.Tensor, alpha: torch.Tensor, scale: torch.Ten
     _check(lib.taco_decompress_blockscale(_ptr(q.contiguous()), _ptr(alpha.contiguous()),
                                           _ptr(scale.contiguous()), T, H, block, _ptr(out),
                                           _stream(dev, stream)))
+    return out
+
+
+def _int8_scales(T: int, H: int, block: int) -> int:
+    if block == 0:
+        return 1
+    if block not in (64, 128, 256) or H % block:
+        _check(4 if block not in (64, 128, 256) else 3)
+    return T * (H // block)
+
+
+def compress_int8(x: torch.Tensor, block: int = 0, *, q: torch.Tensor | None = None,
+                  scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                  stream=None):
+    """INT8 degrade path: symmetric absmax INT8 of a bf16 [tokens, hidden] GPU
+    tensor, one scale per tensor (block 0) or per block of `block` elements.
+    Returns (q int8 [tokens, hidden], scale float32 [1] or [tokens, hidden/block])."""
+    lib = load()
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    dev = _require_gpu(x)
+    x = x.contiguous()
+    T, H = x.shape
+    n = _int8_scales(T, H, block)
+    if q is None:
+        q = torch.empty((T, H), dtype=torch.int8, device=dev)
+    if scale is None:
+        scale = torch.empty((1,) if block == 0 else (T, H // block), dtype=torch.float32, device=dev)
+    _require_gpu(x, q, scale)
+    _require_buffer(q, "q", torch.int8, T * H, (T, H))
+    _require_buffer(scale, "scale", torch.float32, n)
+    nbytes = 0
+    if block == 0:
+        need = lib.taco_compress_int8_workspace_bytes(T, H, 0)
+        if workspace is None:
+            workspace = _workspace(dev, need)
+        _require_gpu(workspace)
+        if not workspace.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.taco_compress_int8(_ptr(x), T, H, block, _ptr(q), _ptr(scale), _ptr(workspace), nbytes,
+                                  _stream(dev, stream)))
+    return q, scale
+
+
+def decompress_int8(q: torch.Tensor, scale: torch.Tensor, block: int = 0, *,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Inverse of compress_int8 with the same block: bf16 [tokens, hidden]."""
+    lib = load()
+    if q.dim() != 2 or q.dtype != torch.int8:
+        raise ValueError("q must be a 2-D int8 tensor")
+    if scale.dtype != torch.float32:
+        raise ValueError("scale must be float32")
+    dev = _require_gpu(q, scale)
+    T, H = q.shape
+    if scale.numel() != _int8_scales(T, H, block):
+        raise ValueError("scale needs one element per tensor (block 0) or per block")
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _require_gpu(q, out)
+    _require_buffer(out, "out", torch.bfloat16, T * H, (T, H))
+    _check(lib.taco_decompress_int8(_ptr(q.contiguous()), _ptr(scale.contiguous()), T, H, block, _ptr(out),
+                                    _stream(dev, stream)))
     return out
 
 

@@ -118,6 +118,14 @@ __device__ __forceinline__ void store16(uint4* p, const uint4 v) {
 }
 
 template <bool NT>
+__device__ __forceinline__ void store8(uint2* p, const uint2 v) {
+  if constexpr (NT)
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x2_t, v), reinterpret_cast<u32x2_t*>(p));
+  else
+    *p = v;
+}
+
+template <bool NT>
 __device__ __forceinline__ uint4 load16(const uint4* p) {
   if constexpr (NT)
     return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
@@ -1176,6 +1184,160 @@ __global__ __launch_bounds__(64 * WAVES) void compress_streaming_kernel(
     if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
 }
 
+// ============================================================== INT8 degrade path
+//
+// Symmetric absmax INT8: the comparator the pages argue against [TACO
+// pt-summary, sections 1 and 2.A: uniform INT8 steps send the dense
+// near-zero values of TP tensors to the same integer] and a fallback for
+// consumers without FP8.  A = max|x| over the tensor or over a block of B
+// consecutive elements of a row, s = fp32(127 / A) (1 if A = 0),
+// code = clamp(rne(fp32(x s)), +-127), x_hat = bf16(fp32(code * fp32(1 / s))).
+// No ASH and no rotation.  Streaming kernels: each lane owns 8 consecutive
+// bf16 values (one 16-byte load) and their 8 codes (one 8-byte store); a
+// workgroup covers kInt8Unroll x 256 consecutive 16-byte pieces per trip.
+
+constexpr int kInt8Unroll = 4;
+
+// max |x| of 8 bf16 values as a bf16 bit pattern (non-negative bf16 values
+// order like their bits).
+__device__ __forceinline__ unsigned bf16x8_absmax_bits(const uint4 v) {
+  const unsigned a = max(v.x & 0x7FFFu, (v.x >> 16) & 0x7FFFu);
+  const unsigned b = max(v.y & 0x7FFFu, (v.y >> 16) & 0x7FFFu);
+  const unsigned c = max(v.z & 0x7FFFu, (v.z >> 16) & 0x7FFFu);
+  const unsigned d = max(v.w & 0x7FFFu, (v.w >> 16) & 0x7FFFu);
+  return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ float int8_scale_of(float amax) {
+  return amax == 0.0f ? 1.0f : 127.0f / amax;
+}
+
+// The two int8 codes of the bf16 pair in w, in the low 16 bits (element 0 first).
+__device__ __forceinline__ unsigned int8_pair(unsigned w, float s) {
+  const float lo = fminf(fmaxf(__builtin_rintf(__uint_as_float(w << 16) * s), -127.0f), 127.0f);
+  const float hi = fminf(fmaxf(__builtin_rintf(__uint_as_float(w & 0xFFFF0000u) * s), -127.0f), 127.0f);
+  return (static_cast<unsigned>(static_cast<int>(lo)) & 0xFFu) |
+         ((static_cast<unsigned>(static_cast<int>(hi)) & 0xFFu) << 8);
+}
+
+__device__ __forceinline__ uint2 int8_codes_bf16x8(const uint4 v, float s) {
+  return make_uint2(int8_pair(v.x, s) | (int8_pair(v.y, s) << 16), int8_pair(v.z, s) | (int8_pair(v.w, s) << 16));
+}
+
+__device__ __forceinline__ uint4 bf16x8_from_int8x8(const uint2 c, float r) {
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    v[j] = static_cast<float>(static_cast<int8_t>((c.x >> (8 * j)) & 0xFFu));
+    v[4 + j] = static_cast<float>(static_cast<int8_t>((c.y >> (8 * j)) & 0xFFu));
+  }
+  return to_bf16x8(v, r);
+}
+
+// Per-tensor INT8, pass 1: each workgroup's max |x| into partial[blockIdx.x].
+__global__ __launch_bounds__(kThreads) void int8_absmax_kernel(const uint4* __restrict__ x, int64_t n16,
+                                                               float* __restrict__ partial) {
+  __shared__ float red[kWaves];
+  unsigned m = 0;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads * kInt8Unroll;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kInt8Unroll; base < n16; base += stride) {
+    uint4 v[kInt8Unroll];
+#pragma unroll
+    for (int u = 0; u < kInt8Unroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      v[u] = i < n16 ? x[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kInt8Unroll; ++u) m = max(m, bf16x8_absmax_bits(v[u]));
+  }
+  const float wg = workgroup_max<kWaves>(__uint_as_float(m << 16), red);
+  if (threadIdx.x == 0) partial[blockIdx.x] = wg;
+}
+
+// Per-tensor INT8, pass 2: every workgroup folds the partial maxima into s,
+// then converts its pieces.
+__global__ __launch_bounds__(kThreads) void int8_quant_tensor_kernel(
+    const uint4* __restrict__ x, int64_t n16, const float* __restrict__ partial, int npartial,
+    float* __restrict__ scale, uint2* __restrict__ q) {
+  __shared__ float red[kWaves];
+  float m = 0.0f;
+  for (int p = threadIdx.x; p < npartial; p += kThreads) m = fmaxf(m, partial[p]);
+  const float s = int8_scale_of(workgroup_max<kWaves>(m, red));
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads * kInt8Unroll;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kInt8Unroll; base < n16; base += stride) {
+    uint4 v[kInt8Unroll];
+#pragma unroll
+    for (int u = 0; u < kInt8Unroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      v[u] = i < n16 ? x[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kInt8Unroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      if (i < n16) store8<TACO_NT_CODE_STORES != 0>(&q[i], int8_codes_bf16x8(v[u], s));
+    }
+  }
+}
+
+// Per-block INT8: a block spans G = B / 8 consecutive lanes (G divides 64 and
+// every trip starts on a wavefront boundary, so no block straddles two
+// wavefronts); its max is an xor-shuffle over the group.  The trip loop is
+// uniform over the workgroup, and a group lies entirely inside or outside
+// the tensor, so the shuffles only read lanes of the same, valid group.
+template <int G>
+__global__ __launch_bounds__(kThreads) void int8_quant_block_kernel(
+    const uint4* __restrict__ x, int64_t n16, float* __restrict__ scale, uint2* __restrict__ q) {
+  const int lane = threadIdx.x & 63;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads * kInt8Unroll;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kInt8Unroll; base < n16; base += stride) {
+    uint4 v[kInt8Unroll];
+#pragma unroll
+    for (int u = 0; u < kInt8Unroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      v[u] = i < n16 ? x[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kInt8Unroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      unsigned m = bf16x8_absmax_bits(v[u]);
+#pragma unroll
+      for (int o = 1; o < G; o <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), o)));
+      const float s = int8_scale_of(__uint_as_float(m << 16));
+      if (i < n16) {
+        store8<TACO_NT_CODE_STORES != 0>(&q[i], int8_codes_bf16x8(v[u], s));
+        if (lane % G == 0) scale[i / G] = s;
+      }
+    }
+  }
+}
+
+// INT8 decompress.  G = B / 8 lanes per scale block, or 0 for one scale per
+// tensor.
+template <int G>
+__global__ __launch_bounds__(kThreads) void int8_dequant_kernel(
+    const uint2* __restrict__ q, const float* __restrict__ scale, int64_t n16, uint4* __restrict__ out) {
+  const float r0 = G == 0 ? 1.0f / *scale : 1.0f;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads * kInt8Unroll;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kInt8Unroll; base < n16; base += stride) {
+    uint2 c[kInt8Unroll];
+    float sk[kInt8Unroll];
+#pragma unroll
+    for (int u = 0; u < kInt8Unroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      c[u] = i < n16 ? q[i] : make_uint2(0, 0);
+      if constexpr (G != 0) sk[u] = i < n16 ? scale[i / G] : 1.0f;
+      else sk[u] = 1.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kInt8Unroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      const float r = G == 0 ? r0 : 1.0f / sk[u];
+      if (i < n16) store16<TACO_NT_OUT_STORES != 0>(&out[i], bf16x8_from_int8x8(c[u], r));
+    }
+  }
+}
+
 // ----------------------------------------------------------------- host side
 
 int device_cu_count() {
@@ -1370,6 +1532,53 @@ void launch_compress_streaming(const void* x, int64_t nblocks, float energy, con
                      reinterpret_cast<unsigned*>(amax_out), reinterpret_cast<uint4*>(q));
 }
 
+// Workgroups of the INT8 streaming kernels (kInt8Unroll pieces per thread per
+// trip), at most cap.
+int int8_grid(int64_t n16, int64_t cap) {
+  const int64_t per = static_cast<int64_t>(kThreads) * kInt8Unroll;
+  return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>((n16 + per - 1) / per, cap)));
+}
+
+taco_status_t check_shape_int8(int64_t tokens, int64_t hidden, int32_t block) {
+  if (block != 0) return check_shape(tokens, hidden, block);
+  if (tokens < 1 || hidden < 1 || hidden % 8 != 0) return TACO_ERR_SHAPE;
+  if (tokens > (int64_t(1) << 40) / hidden) return TACO_ERR_SHAPE;
+  return TACO_OK;
+}
+
+void launch_compress_int8(const void* x, int64_t n16, int32_t block, int8_t* q, float* scale,
+                          void* workspace, hipStream_t stream) {
+  const uint4* xv = static_cast<const uint4*>(x);
+  uint2* qv = reinterpret_cast<uint2*>(q);
+  const int g = int8_grid(n16, INT32_MAX);
+  switch (block) {
+    case 0: {
+      float* partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kPartialOffset);
+      const int g1 = int8_grid(n16, kMaxPartials);
+      hipLaunchKernelGGL(int8_absmax_kernel, dim3(g1), dim3(kThreads), 0, stream, xv, n16, partial);
+      hipLaunchKernelGGL(int8_quant_tensor_kernel, dim3(g), dim3(kThreads), 0, stream, xv, n16, partial, g1,
+                         scale, qv);
+      break;
+    }
+    case 64: hipLaunchKernelGGL(int8_quant_block_kernel<8>, dim3(g), dim3(kThreads), 0, stream, xv, n16, scale, qv); break;
+    case 128: hipLaunchKernelGGL(int8_quant_block_kernel<16>, dim3(g), dim3(kThreads), 0, stream, xv, n16, scale, qv); break;
+    default: hipLaunchKernelGGL(int8_quant_block_kernel<32>, dim3(g), dim3(kThreads), 0, stream, xv, n16, scale, qv); break;
+  }
+}
+
+void launch_decompress_int8(const int8_t* q, const float* scale, int64_t n16, int32_t block, void* out,
+                            hipStream_t stream) {
+  const uint2* qv = reinterpret_cast<const uint2*>(q);
+  uint4* ov = static_cast<uint4*>(out);
+  const int g = int8_grid(n16, INT32_MAX);
+  switch (block) {
+    case 0: hipLaunchKernelGGL(int8_dequant_kernel<0>, dim3(g), dim3(kThreads), 0, stream, qv, scale, n16, ov); break;
+    case 64: hipLaunchKernelGGL(int8_dequant_kernel<8>, dim3(g), dim3(kThreads), 0, stream, qv, scale, n16, ov); break;
+    case 128: hipLaunchKernelGGL(int8_dequant_kernel<16>, dim3(g), dim3(kThreads), 0, stream, qv, scale, n16, ov); break;
+    default: hipLaunchKernelGGL(int8_dequant_kernel<32>, dim3(g), dim3(kThreads), 0, stream, qv, scale, n16, ov); break;
+  }
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------- C ABI
@@ -1509,7 +1718,37 @@ taco_status_t taco_decompress_sum(const uint8_t* const* q_fp8, const float* cons
   return launched();
 }
 
-}  // extern "C"
+size_t taco_compress_int8_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block) {
+  if (check_shape_int8(tokens, hidden, block) != TACO_OK) return 0;
+  return block == 0 ? kCompressWorkspace : 0;
+}
+
+taco_status_t taco_compress_int8(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,
+                                 int8_t* q_int8, float* scale, void* workspace, size_t workspace_bytes,
+                                 taco_stream_t stream) {
+  if (!x_bf16 || !q_int8 || !scale || (block == 0 && !workspace)) return TACO_ERR_NULL;
+  const taco_status_t st = check_shape_int8(tokens, hidden, block);
+  if (st != TACO_OK) return st;
+  if (!aligned(x_bf16, 16) || !aligned(q_int8, 16) || !aligned(scale, 4) ||
+      (block == 0 && !aligned(workspace, 256)))
+    return TACO_ERR_ALIGN;
+  if (block == 0 && workspace_bytes < kCompressWorkspace) return TACO_ERR_WORKSPACE;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  launch_compress_int8(x_bf16, tokens * hidden / 8, block, q_int8, scale, workspace,
+                       reinterpret_cast<hipStream_t>(stream));
+  return launched();
+}
+
+taco_status_t taco_decompress_int8(const int8_t* q_int8, const float* scale, int64_t tokens, int64_t hidden,
+                                   int32_t block, void* y_bf16, taco_stream_t stream) {
+  if (!q_int8 || !scale || !y_bf16) return TACO_ERR_NULL;
+  const taco_status_t st = check_shape_int8(tokens, hidden, block);
+  if (st != TACO_OK) return st;
+  if (!aligned(q_int8, 16) || !aligned(y_bf16, 16) || !aligned(scale, 4)) return TACO_ERR_ALIGN;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  launch_decompress_int8(q_int8, scale, tokens * hidden / 8, block, y_bf16, reinterpret_cast<hipStream_t>(stream));
+  return launched();
+}
 
 size_t taco_decompress_sum_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block) {
   if (check_shape(tokens, hidden, block) != TACO_OK) return 0;
@@ -1611,3 +1850,5 @@ taco_status_t taco_compress_delayed(const void* x_bf16, int64_t tokens, int64_t 
   }
   return launched();
 }
+
+}  // extern "C"

@@ -257,6 +257,44 @@ taco_status_t taco_compress_delayed(const void* x_bf16, int64_t tokens, int64_t 
                                     uint8_t* q_fp8, float* alpha, float* scale, float* amax_out,
                                     taco_stream_t stream);
 
+/*
+ * INT8 degrade path: symmetric absmax INT8, the quantiser the pages compare
+ * FP8 against [TACO pt-summary, sections 1 and 2.A: uniform INT8 steps map
+ * the dense near-zero values of TP tensors to the same integer].  No ASH and
+ * no rotation.  The pages give no INT8 arithmetic; this library uses
+ *   A     = max |x| over the tensor (block == 0) or over each block of
+ *           `block` consecutive elements of a row (block in {64, 128, 256})
+ *   s     = fp32(127 / A), 1 if A == 0
+ *   code  = clamp(round_half_even(fp32(x * s)), -127, 127)
+ *   x_hat = bf16_RNE(fp32(code * fp32(1 / s)))
+ * with every product and quotient rounded to fp32 once.
+ *
+ *   x_bf16     in : bf16 [tokens, hidden], 16-byte aligned; hidden % 8 == 0
+ *                   when block == 0, hidden % block == 0 otherwise
+ *   q_int8     out: int8 [tokens, hidden], 16-byte aligned
+ *   scale      out: fp32 [1] (block == 0) or [tokens, hidden / block]
+ *   workspace  block == 0: device scratch of at least
+ *              taco_compress_int8_workspace_bytes() bytes, 256-byte aligned
+ *              (it holds per-workgroup maxima; no zero-fill needed; a
+ *              taco_compress workspace may be passed, its barrier state is
+ *              not touched).  Ignored (may be NULL) for block != 0.
+ * Errors: TACO_ERR_NULL, TACO_ERR_SHAPE, TACO_ERR_UNSUPPORTED_BLOCK (block
+ * not in {0, 64, 128, 256}), TACO_ERR_ALIGN, TACO_ERR_WORKSPACE,
+ * TACO_ERR_HIP.  Per-tensor calls are two kernels (maxima, then codes), so
+ * x is read twice; per-block calls are one.
+ */
+size_t taco_compress_int8_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block);
+taco_status_t taco_compress_int8(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,
+                                 int8_t* q_int8, float* scale, void* workspace,
+                                 size_t workspace_bytes, taco_stream_t stream);
+
+/* INT8 decompress: y_bf16 (bf16 [tokens, hidden], 16-byte aligned) from the
+ * codes and the scale(s) of taco_compress_int8 with the same block (0: one
+ * scale per tensor).  Same errors, no workspace. */
+taco_status_t taco_decompress_int8(const int8_t* q_int8, const float* scale, int64_t tokens,
+                                   int64_t hidden, int32_t block, void* y_bf16,
+                                   taco_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -116,3 +116,26 @@ def test_argument_checks_fail_before_any_launch(lib):
     assert dsc(arr, arr, arr, 0, 8, 128, 64, f, other, other, other, FAKE, ws2, None) == 7
     assert dsc(arr, arr, arr, 1, 8, 128, 64, ctypes.c_float(-1.0), other, other, other, FAKE, ws2, None) == 5
     assert dsc(arr, arr, arr, 1, 8, 128, 64, f, other, None, other, FAKE, ws2, None) == 1
+
+
+def test_int8_argument_checks_fail_before_any_launch(lib):
+    ws = lib.taco_compress_int8_workspace_bytes(8, 128, 0)
+    assert ws == lib.taco_compress_workspace_bytes(8, 128, 64)      # same region layout
+    assert lib.taco_compress_int8_workspace_bytes(8, 128, 128) == 0  # per block: none needed
+    assert lib.taco_compress_int8_workspace_bytes(8, 12, 0) == 0     # hidden % 8 != 0
+    assert lib.taco_compress_int8_workspace_bytes(8, 96, 64) == 0
+    c = lib.taco_compress_int8
+    assert c(None, 8, 128, 0, FAKE, FAKE, FAKE, ws, None) == 1
+    assert c(FAKE, 8, 128, 0, FAKE, FAKE, None, ws, None) == 1       # per tensor needs a workspace
+    assert c(FAKE, 8, 12, 0, FAKE, FAKE, FAKE, ws, None) == 3
+    assert c(FAKE, 0, 128, 0, FAKE, FAKE, FAKE, ws, None) == 3
+    assert c(FAKE, 8, 96, 64, FAKE, FAKE, None, 0, None) == 3
+    assert c(FAKE, 8, 128, 32, FAKE, FAKE, None, 0, None) == 4
+    assert c(FAKE + 8, 8, 128, 0, FAKE, FAKE, FAKE, ws, None) == 2
+    assert c(FAKE, 8, 128, 0, FAKE, FAKE, FAKE + 16, ws, None) == 2   # workspace not 256-aligned
+    assert c(FAKE, 8, 128, 0, FAKE, FAKE, FAKE, ws - 4, None) == 6
+    d = lib.taco_decompress_int8
+    assert d(None, FAKE, 8, 128, 0, FAKE, None) == 1
+    assert d(FAKE, FAKE, 8, 128, 16, FAKE, None) == 4
+    assert d(FAKE, FAKE, 8, 100, 0, FAKE, None) == 3
+    assert d(FAKE, FAKE, 8, 128, 0, FAKE + 8, None) == 2
