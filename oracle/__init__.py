@@ -9,6 +9,7 @@ from .int8 import (  # noqa: F401
     decompress_int8,
     decompress_int8_f64,
     int8_scale,
+    quantize_int8,
 )
 from .taco_oracle import (  # noqa: F401
     Q_MAX,

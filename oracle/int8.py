@@ -46,6 +46,12 @@ def _x32(x_bits: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16)).astype(np.float32)   # exact
 
 
+def quantize_int8(x_bits: np.ndarray, s) -> np.ndarray:
+    """Codes of x under a given per-tensor scale s (the second half of
+    compress_int8_tensor, for tensors whose maximum is known elsewhere)."""
+    return _codes(_x32(x_bits), np.float32(s))
+
+
 def compress_int8_tensor(x_bits: np.ndarray):
     """Per-tensor absmax INT8: (codes int8 [T, H], s float32)."""
     x = _x32(x_bits)

@@ -125,3 +125,12 @@ def test_round_trip_error_bound(block):
     assert np.all(np.abs(exact - xv) <= 0.5 / se * (1 + 2.0 ** -15))
     got = oracle.bf16_bits_to_f64(oracle.decompress_int8(q, s, block))
     assert np.all(np.abs(got - exact) <= 2.0 ** -8 * np.abs(exact) * (1 + 2.0 ** -20))
+
+
+def test_quantize_int8_is_the_second_half_of_compress():
+    x = W.bf16_bits(W.make("tiny", seed=13, tokens=3))
+    q, s = oracle.compress_int8_tensor(x)
+    assert np.array_equal(oracle.quantize_int8(x, s), q)
+    # a larger given scale saturates at +-127
+    q2 = oracle.quantize_int8(x, s * 4)
+    assert np.max(np.abs(q2.astype(int))) == 127
