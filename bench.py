@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "compress/decompress GB/s (bf16 in) and % of MI355X HBM peak, 1 GPU"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
 WORKLOAD = "gpt3_6p7b"
 TOKENS, HIDDEN, BLOCK, NPARTS = 4096, 4096, 128, 4
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "compress_gpt3_6p7b_counters.json")
@@ -74,17 +75,18 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per compress call from the committed rocprofv3 counter run,
-    or None if the kernel source changed since the counters were taken."""
+def measured_counters():
+    """The committed rocprofv3 counter run of the compress kernel (HBM bytes
+    and MFMA instructions per call), or {} if the kernel source changed since
+    the counters were taken."""
     try:
         with open(COUNTERS_FILE) as f:
             c = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     if c.get("kernel_source_sha256") != kernel_source_hash():
-        return None
-    return c.get("traffic_bytes_per_call")
+        return {}
+    return c
 
 
 def cpu_baseline(rows: int, min_seconds: float):
@@ -289,17 +291,55 @@ def main():
     avg_us = {}
     extra = ["decompress_sum_compress", "compress_blockscale", "decompress_blockscale", "compress_delayed",
              "compress_int8_tensor", "decompress_int8_tensor", "compress_int8_block", "decompress_int8_block"]
-    for op in ops + extra:
-        g, calls = op_graphs[op]
+    def time_us(fn, calls, repeat):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(reps):
-            g.replay()
+        for _ in range(repeat):
+            fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        avg_us[op] = 1e3 * e0.elapsed_time(e1) / (reps * calls)
+        return 1e3 * e0.elapsed_time(e1) / (repeat * calls)
+
+    for op in ops + extra:
+        g, calls = op_graphs[op]
+        avg_us[op] = time_us(g.replay, calls, reps)
+
+    # ---- warm: the step's ops back to back on one buffer set, whose inputs stay
+    # in the 256 MB Infinity Cache (reported apart, labeled; not the metric)
+    s0 = sets[0]
+    warm = {"compress": (capture(lambda: [op_compress(s0, k) for _ in range(8) for k in range(2)]), 16),
+            "decompress": (capture(lambda: [op_decompress(s0, k) for _ in range(8) for k in range(2)]), 16),
+            "decompress_sum": (capture(lambda: [op_sum(s0) for _ in range(16)]), 16)}
+    warm_us = {}
+    for op, (g, calls) in warm.items():
+        g.replay()
+        warm_us[op] = time_us(g.replay, calls, reps)
+    del warm
+
+    # ---- 32 decompress-sum layers back to back (4 parts of [4096, 4096] at block
+    # 256, part p drawn with seed p, in 32 distinct layer slots: 2.2 GB of codes):
+    # per-layer time of eager launches against the same 32 calls in one graph;
+    # the difference is the launch gap.
+    B5, L5 = 256, 32
+    src5 = [tuple(t.clone() for t in taco.compress(W.make("dsum_part", seed=p).to(dev), B5))
+            for p in range(NPARTS)]
+    slots5 = [[tuple(t.clone() for t in part) for part in src5] for _ in range(L5)]
+    outs5 = [torch.empty((TOKENS, HIDDEN), dtype=torch.bfloat16, device=dev) for _ in range(L5)]
+    del src5
+
+    def layers():
+        for layer in range(L5):
+            taco.decompress_sum(slots5[layer], B5, out=outs5[layer])
+
+    layers()
+    eager_us = time_us(layers, L5, 3)
+    g5 = capture(layers)
+    g5.replay()
+    graph_us = time_us(g5.replay, L5, 3)
+    del g5, slots5, outs5
+    torch.cuda.empty_cache()
 
     N = TOKENS * HIDDEN
     bf16_bytes_step = 2 * N * 5
@@ -318,7 +358,19 @@ def main():
         "decompress_int8_block": 3 * N + 4 * nscales,
     }
     achieved = alg["compress"] / (avg_us["compress"] * 1e-6) / 1e9
-    traffic = measured_traffic()
+    counters = measured_counters()
+    traffic = counters.get("traffic_bytes_per_call")
+    mfma_insts = counters.get("mfma_instructions_per_call")
+    mfma = None
+    if mfma_insts:
+        # v_mfma_f32_16x16x32_bf16: 16 x 16 x 32 multiply-adds per instruction
+        executed = mfma_insts * 16 * 16 * 32 * 2 / (avg_us["compress"] * 1e-6) / 1e12
+        dense = 2 * BLOCK * N / (avg_us["compress"] * 1e-6) / 1e12
+        mfma = {"instructions_per_call": mfma_insts,
+                "executed_TFLOPs": round(executed, 1),
+                "dense_contraction_TFLOPs": round(dense, 1),
+                "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                "frac": round(executed / MFMA_BF16_PEAK_TFLOPS, 4)}
 
     out = {
         "metric": METRIC,
@@ -353,6 +405,7 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes": alg["compress"],
             "avg_us": round(avg_us["compress"], 3),
+            "mfma": mfma,
         },
         "ops": {
             op: {"avg_us": round(avg_us[op], 3),
@@ -370,6 +423,15 @@ def main():
         "extra_ops_note": "not part of the step: decompress_sum_compress (4 parts -> FP8 of their bf16 "
                           "sum), the per-block-guard and delayed-scale Dual-Scale variants, and the INT8 "
                           "degrade path (absmax per tensor: two kernels, x read twice; per 128-block)",
+        "warm_ops": {op: {"avg_us": round(v, 3),
+                          "algorithmic_GBps": round(alg[op] / (v * 1e-6) / 1e9, 1)} for op, v in warm_us.items()},
+        "warm_ops_note": "Infinity-Cache resident: back-to-back calls on one buffer set; not the metric",
+        "decompress_sum_32_layers": {
+            "block": B5, "parts": NPARTS, "layers": L5,
+            "us_per_layer_eager_launches": round(eager_us, 3),
+            "us_per_layer_one_graph": round(graph_us, 3),
+            "launch_gap_us_per_layer": round(eager_us - graph_us, 3),
+            "algorithmic_GBps_one_graph": round((NPARTS * (N + 4 * (N // B5) + 4) + 2 * N) / (graph_us * 1e-6) / 1e9, 1)},
         "wall_s_timed": round(t_wall, 4),
         "timing": "steps replayed as HIP graphs of one step per buffer set (each step all 5 calls); per-op "
                   f"figures from graphs of back-to-back calls, {OP_PASSES} passes over all buffer sets",
