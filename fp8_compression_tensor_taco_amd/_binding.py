@@ -37,7 +37,7 @@ class TacoError(RuntimeError):
 
 _lib = None
 _lock = threading.Lock()
-_workspaces: dict[tuple[int, str], torch.Tensor] = {}
+_workspaces: dict[tuple[int, str, int], torch.Tensor] = {}
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -194,13 +194,16 @@ def get_barrier_spin_limit() -> int:
 def workspace_timed_out(workspace: torch.Tensor | None = None, stream=None) -> bool:
     """Whether a single-pass call on `workspace` has given up at its grid
     barrier since the workspace was zero-filled (waits for the stream).  With
-    no argument, checks every workspace the binding has allocated."""
+    no argument, checks every workspace the binding has allocated, each after
+    waiting for the stream it serves."""
     lib = load()
-    wss = [workspace] if workspace is not None else list(_workspaces.values())
-    for ws in wss:
-        dev = _require_gpu(ws)
+    if workspace is not None:
+        checks = [(workspace, _stream(_require_gpu(workspace), stream))]
+    else:
+        checks = [(ws, key[2]) for key, ws in _workspaces.items()]   # each on its own stream
+    for ws, handle in checks:
         flag = ctypes.c_int(0)
-        _check(lib.taco_workspace_timed_out(_ptr(ws), _stream(dev, stream), ctypes.byref(flag)))
+        _check(lib.taco_workspace_timed_out(_ptr(ws), handle, ctypes.byref(flag)))
         if flag.value:
             return True
     return False
@@ -214,14 +217,20 @@ def workspace_bytes(tokens: int, hidden: int, block: int) -> int:
     return int(load().taco_compress_workspace_bytes(tokens, hidden, block))
 
 
-def _workspace(device: torch.device, nbytes: int, kind: str = "compress") -> torch.Tensor:
-    """A zero-filled workspace per device and kind, grown when too small (a new
-    one starts zeroed, as the library requires)."""
+def _workspace(device: torch.device, nbytes: int, kind: str, stream_handle: int) -> torch.Tensor:
+    """A zero-filled workspace per device, kind and stream, grown when too
+    small (a new one starts zeroed, as the library requires).  Calls on one
+    stream are ordered, so they may share it; calls on different streams get
+    different workspaces, since concurrent calls on one workspace race."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _workspaces.get((idx, kind))
+    key = (idx, kind, int(stream_handle or 0))
+    ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
-        _workspaces[(idx, kind)] = ws
+        current = torch.cuda.current_stream(device)
+        if int(current.cuda_stream) != key[2]:
+            current.synchronize()       # the zero-fill ran on another stream than the call's
+        _workspaces[key] = ws
     return ws
 
 
@@ -251,7 +260,7 @@ def compress(x: torch.Tensor, block: int, target_energy: float = 1.0, *,
         scale = torch.empty((1,), dtype=torch.float32, device=dev)
     need = lib.taco_compress_workspace_bytes(T, H, block)
     if workspace is None:
-        workspace = _workspace(dev, need)
+        workspace = _workspace(dev, need, "compress", _stream(dev, stream))
     _require_gpu(x, q, alpha, scale, workspace)
     _require_buffer(q, "q", torch.uint8, T * H, (T, H))
     _require_buffer(alpha, "alpha", torch.float32, n)
@@ -324,7 +333,7 @@ def decompress_sum_compress(parts, block: int, target_energy: float = 1.0, *,
         scale = torch.empty((1,), dtype=torch.float32, device=dev)
     need = lib.taco_decompress_sum_compress_workspace_bytes(T, H, block)
     if workspace is None:
-        workspace = _workspace(dev, need, "decompress_sum_compress")
+        workspace = _workspace(dev, need, "decompress_sum_compress", _stream(dev, stream))
     _require_gpu(parts[0][0], q, alpha, scale, workspace)
     _require_buffer(q, "q", torch.uint8, T * H, (T, H))
     _require_buffer(alpha, "alpha", torch.float32, n)
@@ -464,7 +473,7 @@ def compress_int8(x: torch.Tensor, block: int = 0, *, q: torch.Tensor | None = N
     if block == 0:
         need = lib.taco_compress_int8_workspace_bytes(T, H, 0)
         if workspace is None:
-            workspace = _workspace(dev, need)
+            workspace = _workspace(dev, need, "compress", _stream(dev, stream))
         _require_gpu(workspace)
         if not workspace.is_contiguous():
             raise ValueError("workspace must be contiguous")

@@ -1389,7 +1389,7 @@ int resident_grid(Kernel kernel, int threads) {
 
 taco_status_t launched() { return hipGetLastError() == hipSuccess ? TACO_OK : TACO_ERR_HIP; }
 
-int g_engine = TACO_ENGINE_AUTO;   // rotation engine of taco_compress (process-wide)
+std::atomic<int> g_engine{TACO_ENGINE_AUTO};   // rotation engine of taco_compress (process-wide)
 std::atomic<unsigned> g_spin_limit{kDefaultSpinLimit};   // barrier poll bound (process-wide)
 
 // Launches the fused compress with TPW tiles per wavefront if every one of its
@@ -1421,7 +1421,7 @@ bool launch_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, 
   return false;
 }
 
-bool g_single_pass = true;   // fused compress when the tensor fits (process-wide)
+std::atomic<bool> g_single_pass{true};   // fused compress when the tensor fits (process-wide)
 
 template <int B>
 void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, float* alpha,
@@ -1432,7 +1432,7 @@ void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, f
   char* ws = static_cast<char*>(workspace);
   float* partial = reinterpret_cast<float*>(ws + kPartialOffset);
   // Single fused pass when the tensor fits in the resident wavefronts' VGPRs.
-  if (g_single_pass && launch_fused<B>(xv, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
+  if (g_single_pass.load() && launch_fused<B>(xv, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
   constexpr int U = 2;
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t per_wg = static_cast<int64_t>(kWaves) * U;
@@ -1504,7 +1504,7 @@ void launch_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblo
   // 16 wavefronts per CU (128 VGPRs each) up to B = 128; at B = 256 the
   // rotation of the sum needs more registers, so 8 wavefronts (256 VGPRs),
   // two tiles each.
-  if (g_single_pass) {
+  if (g_single_pass.load()) {
     if constexpr (B <= 128) {
       if (try_decompress_sum_compress<B, 1, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
       if (try_decompress_sum_compress<B, 2, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
@@ -1610,15 +1610,15 @@ taco_status_t taco_set_rotation_engine(taco_engine_t engine) {
   // remains.
   if (engine == TACO_ENGINE_VALU) return TACO_ERR_BAD_ENGINE;
   if (engine != TACO_ENGINE_AUTO && engine != TACO_ENGINE_MFMA) return TACO_ERR_BAD_ENGINE;
-  g_engine = engine;
+  g_engine.store(engine);
   return TACO_OK;
 }
 
-taco_engine_t taco_get_rotation_engine(void) { return static_cast<taco_engine_t>(g_engine); }
+taco_engine_t taco_get_rotation_engine(void) { return static_cast<taco_engine_t>(g_engine.load()); }
 
-void taco_set_single_pass(int enable) { g_single_pass = enable != 0; }
+void taco_set_single_pass(int enable) { g_single_pass.store(enable != 0); }
 
-int taco_get_single_pass(void) { return g_single_pass ? 1 : 0; }
+int taco_get_single_pass(void) { return g_single_pass.load() ? 1 : 0; }
 
 void taco_set_barrier_spin_limit(uint32_t polls) {
   g_spin_limit.store(polls == 0 ? kDefaultSpinLimit : polls);

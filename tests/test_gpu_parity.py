@@ -599,3 +599,36 @@ def test_graph_replays_match_eager(taco):
         torch.cuda.synchronize()
     assert int(ws[8:12].cpu().numpy().view(np.uint32)[0]) == 0
     assert int(ws2[8:12].cpu().numpy().view(np.uint32)[0]) == 0
+
+
+def test_default_workspaces_are_per_stream(taco):
+    """Calls on two streams with the binding's default workspaces run
+    concurrently without sharing state: both results equal the single-stream
+    ones bitwise.  Two-kernel path: each call's statistics kernel writes the
+    partial maxima its quantisation kernel reads, so one workspace shared by
+    the two streams would mix them.  (Single-pass calls may not run
+    concurrently at all: each needs every compute unit for its barrier.)"""
+    xa = W.make("gpt3_6p7b_act", seed=21).cuda()
+    xb = W.make("gpt3_6p7b_grad", seed=22).cuda()
+    taco.set_single_pass(False)
+    try:
+        ref_a = [t.clone() for t in taco.compress(xa, 128)]
+        ref_b = [t.clone() for t in taco.compress(xb, 128)]
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        s1.wait_stream(torch.cuda.current_stream())
+        s2.wait_stream(torch.cuda.current_stream())
+        outs = []
+        for _ in range(4):
+            with torch.cuda.stream(s1):
+                oa = taco.compress(xa, 128, stream=s1)
+            with torch.cuda.stream(s2):
+                ob = taco.compress(xb, 128, stream=s2)
+            outs.append((oa, ob))
+        torch.cuda.synchronize()
+    finally:
+        taco.set_single_pass(True)
+    for oa, ob in outs:
+        for r, t in zip(ref_a, oa):
+            assert torch.equal(r, t)
+        for r, t in zip(ref_b, ob):
+            assert torch.equal(r, t)
