@@ -561,50 +561,56 @@ __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
 //
 // Grid barrier.  The launch makes every workgroup resident at once (grid <=
 // occupancy x CUs).  The only value exchanged is the max, so the barrier is
-// built from device-scope atomics alone, with no fences (a device-scope
-// release or acquire would write back or invalidate the whole L2).  Atomics
-// on one address serialise at the memory side, so the workgroups are grouped
-// into leaves of kLeafWgs, each leaf on its own 256-byte line:
-//   leaf line {count (64-bit), maxbits, rel}: rel = (call + 1) << 32 | max bits
-//   root line {count (64-bit), timed_out}
-// The counts never reset: every call adds exactly kLeafWgs to every leaf and
-// kLeaves to the root (the first workgroup of a partial leaf adds the missing
-// arrivals, the first leaf adds the missing leaves, and the completing
-// workgroup advances the leaves this grid does not use), so each arrival's
-// own count tells it the call number, and no state has to be read before
-// arriving.  Lane 0 of wavefront 0 folds the workgroup max into its leaf's
-// maxbits (non-negative floats order like their bit patterns) and only after
-// that atomic has returned adds to the leaf count.  The arrival that completes
-// a leaf adds to the root count; the one that completes the root takes every
-// leaf's max with an atomic exchange against 0 (one lane per leaf; this also
-// clears them for the next call) and writes rel = (call + 1, max) into all
-// kLeaves leaf lines.  Everyone else polls its own leaf's rel.  The poll is
-// bounded (spin_limit polls, set by the host): a workgroup that gives up sets
-// the sticky timed_out flag and takes NaN as the max, so its codes are all
-// E4M3 NaN rather than plausible values under a stale scale.  It has already
-// arrived, so the barrier still completes for the others and the workspace
-// stays consistent for the next call; every wavefront finishes.
+// built from device-scope atomic loads, stores and adds alone, with no fences
+// (a device-scope release or acquire would write back or invalidate the whole
+// L2).  Two parts:
+//  * Call number.  Leaf lines of kLeafWgs workgroups each hold a running
+//    64-bit count that never resets and advances by exactly kLeafWgs per
+//    call: every workgroup adds 1 to its leaf (the first of a partial leaf
+//    also adds the missing arrivals) and workgroup 0 adds kLeafWgs to every
+//    leaf the grid does not use.  A workgroup's own add therefore returns a
+//    value that tells it the call number c, without reading any state first.
+//    It is issued while the workgroup's input loads are in flight, so it is
+//    off the critical path.
+//  * Exchange.  Each workgroup stores (c + 1) << 32 | max bits into its own
+//    slot (one 64-bit store; non-negative floats order like their bits), then
+//    wavefront 0 polls the slots of the whole grid until all of them carry
+//    epoch c + 1 and takes their max.  After the last arrival only that store
+//    and one round of polls remain (the previous protocol's chain of leaf and
+//    root atomics took about 1 us longer per call).  Slots of workgroups
+//    beyond this grid are never read; a slot can only hold epoch c + 1 if it
+//    was written in this call, since epochs only grow (zero-filling the
+//    workspace resets counts and slots together).
+// The poll is bounded (spin_limit polls, set by the host): a workgroup that
+// gives up sets the sticky timed_out flag and takes NaN as the max, so its
+// codes are all E4M3 NaN rather than plausible values under a stale scale.
+// It has already counted itself and stored its slot, so the barrier still
+// completes for the others and the workspace stays consistent for the next
+// call; every wavefront finishes.
 
-constexpr int kLine = 256;               // bytes per barrier line
+constexpr int kLine = 256;               // bytes per leaf line
 constexpr int kLeafWgs = 16;             // workgroups per leaf
 constexpr int kLeaves = 64;              // leaf lines => at most 1024 fused workgroups
 constexpr size_t kPartialOffset = static_cast<size_t>(kLine) * (1 + kLeaves);
+constexpr size_t kSlotOffset = kPartialOffset + kMaxPartials * sizeof(float);
+constexpr int kSlotStride = 16;          // bytes per workgroup slot
 constexpr unsigned kDefaultSpinLimit = 1u << 22;
 
 struct RootLine {
-  unsigned long long count;
+  unsigned long long unused;
   unsigned timed_out;
 };
 
 struct LeafLine {
   unsigned long long count;
-  unsigned maxbits;
-  unsigned pad;
-  unsigned long long rel;
 };
 
 __device__ __forceinline__ LeafLine* leaf_line(char* ws, unsigned l) {
   return reinterpret_cast<LeafLine*>(ws + kLine * (1 + l));
+}
+
+__device__ __forceinline__ unsigned long long* slot_of(char* ws, unsigned wg) {
+  return reinterpret_cast<unsigned long long*>(ws + kSlotOffset + static_cast<size_t>(kSlotStride) * wg);
 }
 
 template <typename T>
@@ -622,64 +628,58 @@ __device__ __forceinline__ T add_agent(T* p, T v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Grid-wide max; called by the 64 lanes of wavefront 0 with the workgroup's
-// max (uniform).  Every lane returns the tensor-wide max, or NaN if this
-// workgroup gave up waiting.
-__device__ float grid_max_wave0(float wg_max, char* __restrict__ ws, unsigned spin_limit) {
+// The call number of this launch on this workspace; called by the 64 lanes
+// of wavefront 0 (lane 0 counts this workgroup into its leaf; in workgroup 0,
+// lane l >= the grid's leaf count advances leaf l).  Only lane 0's value is
+// meaningful; grid_max_wave0 broadcasts it.
+__device__ __forceinline__ unsigned long long count_arrival_wave0(char* __restrict__ ws) {
   const int lane = threadIdx.x & 63;
-  RootLine* root = reinterpret_cast<RootLine*>(ws);
   const unsigned l = blockIdx.x / kLeafWgs;
   const unsigned nleaves = (gridDim.x + kLeafWgs - 1) / kLeafWgs;
-  const unsigned in_leaf = min(static_cast<unsigned>(kLeafWgs), gridDim.x - l * kLeafWgs);
-  LeafLine* lf = leaf_line(ws, l);
   unsigned long long call = 0;
-  unsigned role = 0;   // 0: wait for the release; 2: complete the barrier
   if (lane == 0) {
-    const unsigned prev = __hip_atomic_fetch_max(&lf->maxbits, __float_as_uint(wg_max),
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // prev is a finite float pattern, never ~0u: the add cannot be issued
-    // before the max has returned.
-    unsigned long long inc = prev == ~0u ? 2 : 1;
+    const unsigned in_leaf = min(static_cast<unsigned>(kLeafWgs), gridDim.x - l * kLeafWgs);
+    unsigned long long inc = 1;
     if (blockIdx.x % kLeafWgs == 0) inc += kLeafWgs - in_leaf;
-    const unsigned long long a = add_agent(&lf->count, inc) + inc;
-    call = (a - 1) / kLeafWgs;
-    if (a % kLeafWgs == 0) {
-      const unsigned long long rinc = 1 + (l == 0 ? kLeaves - nleaves : 0);
-      if ((add_agent(&root->count, rinc) + rinc) % kLeaves == 0) role = 2;
-    }
+    call = (add_agent(&leaf_line(ws, l)->count, inc) + inc - 1) / kLeafWgs;
+  } else if (blockIdx.x == 0 && static_cast<unsigned>(lane) >= nleaves) {
+    add_agent(&leaf_line(ws, lane)->count, static_cast<unsigned long long>(kLeafWgs));
   }
-  role = __builtin_amdgcn_readfirstlane(role);
-  call = (static_cast<unsigned long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(call >> 32))) << 32) |
-         __builtin_amdgcn_readfirstlane(static_cast<unsigned>(call));
-  const unsigned long long want = (call + 1) << 32;
-  if (role == 2) {
-    LeafLine* o = leaf_line(ws, lane);          // kLeaves == 64: one leaf per lane
-    unsigned mx = 0;
-    if (lane < static_cast<int>(nleaves)) {
-      mx = __hip_atomic_exchange(&o->maxbits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      store_agent(&o->count, (call + 1) * kLeafWgs);   // unused this call: keep in step
-    }
-#pragma unroll
-    for (int k = 32; k > 0; k >>= 1) mx = max(mx, static_cast<unsigned>(__shfl_xor(static_cast<int>(mx), k)));
-    store_agent(&o->rel, want | mx);
-    return __uint_as_float(mx);
-  }
-  unsigned long long r = 0;
-  if (lane == 0) {
-    unsigned spins = 0;
-    while (((r = load_agent(&lf->rel)) >> 32) != (want >> 32)) {
-      if (++spins >= spin_limit) {
-        store_agent(&root->timed_out, 1u);
-        r = 0x7FC00000u;   // quiet NaN: the codes of this workgroup become NaN
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
-  }
-  return __uint_as_float(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(r)));
+  return call;
 }
-static_assert(kLeaves == 64, "grid_max_wave0 releases one leaf per lane");
+static_assert(kLeaves == 64, "count_arrival_wave0 advances one unused leaf per lane");
+
+// Grid-wide max; called by the 64 lanes of wavefront 0 with the workgroup's
+// max (uniform) and lane 0's call number.  Every lane returns the tensor-wide
+// max, or NaN if this workgroup gave up waiting.
+__device__ float grid_max_wave0(float wg_max, unsigned long long call, char* __restrict__ ws,
+                                unsigned spin_limit) {
+  const int lane = threadIdx.x & 63;
+  const unsigned epoch = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(call)) + 1;
+  if (lane == 0)
+    store_agent(slot_of(ws, blockIdx.x), (static_cast<unsigned long long>(epoch) << 32) | __float_as_uint(wg_max));
+  unsigned m = 0, spins = 0;
+  while (true) {
+    bool ok = true;
+    unsigned mm = 0;
+    for (unsigned j = lane; j < gridDim.x; j += 64) {
+      const unsigned long long v = load_agent(slot_of(ws, j));
+      ok = ok && static_cast<unsigned>(v >> 32) == epoch;
+      mm = max(mm, static_cast<unsigned>(v));
+    }
+    m = mm;
+    if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+    if (++spins >= spin_limit) {
+      if (lane == 0) store_agent(&reinterpret_cast<RootLine*>(ws)->timed_out, 1u);
+      m = 0x7FC00000u;   // quiet NaN: the codes of this workgroup become NaN
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), k)));
+  return __uint_as_float(m);
+}
 
 // Wavefront w of W owns tiles w, w + W, ..., w + (TPW-1) W (those < ntiles).
 template <int B, int TPW, bool HOLD_Y, int WAVES>
@@ -705,6 +705,9 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
     const int64_t t = wid + i * nw;
     load_tile_mfma<B, true>(x, t < ntiles ? t : ntiles - 1, nblocks, xr[i]);
   }
+  // the barrier's call number, counted while the loads are in flight
+  unsigned long long call = 0;
+  if (threadIdx.x < 64) call = count_arrival_wave0(ws);
   f32x4_t y[HOLD_Y ? TPW : 1][NM];
   float al[TPW];
   float amax = 0.0f;
@@ -727,7 +730,7 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
   }
   const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x < 64) {
-    const float A = grid_max_wave0(wg, ws, spin_limit);
+    const float A = grid_max_wave0(wg, call, ws, spin_limit);
     if (threadIdx.x == 0) amax_sh = A;
   }
   __syncthreads();
@@ -1068,7 +1071,10 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
   }
   const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x < 64) {
-    const float A = grid_max_wave0(wg, ws, spin_limit);
+    // counted here rather than at the start: a call number held across the
+    // parts' accumulation made the allocator spill (B = 128, 2 tiles)
+    const unsigned long long call = count_arrival_wave0(ws);
+    const float A = grid_max_wave0(wg, call, ws, spin_limit);
     if (threadIdx.x == 0) amax_sh = A;
   }
   __syncthreads();
@@ -1476,7 +1482,7 @@ void launch_decompress_sum(const Parts& parts, int nparts, int64_t nblocks, void
 // Bytes of the compress workspace proper (barrier lines and partial maxima),
 // rounded up so that the decompress-sum-compress intermediate after it is
 // 256-byte aligned.
-constexpr size_t kCompressWorkspace = (kPartialOffset + kMaxPartials * sizeof(float) + 255) / 256 * 256;
+constexpr size_t kCompressWorkspace = (kSlotOffset + kSlotStride * kLeaves * kLeafWgs + 255) / 256 * 256;
 
 template <int B, int TPW, int WAVES>
 bool try_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblocks, float sqrt_eb,
@@ -1646,7 +1652,7 @@ int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block) {
 
 size_t taco_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block) {
   if (check_shape(tokens, hidden, block) != TACO_OK) return 0;
-  return kPartialOffset + static_cast<size_t>(kMaxPartials) * sizeof(float);
+  return kCompressWorkspace;   // leaf lines, partial maxima and barrier slots
 }
 
 taco_status_t taco_compress(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,

@@ -111,8 +111,9 @@ int taco_get_single_pass(void);
 int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block);
 
 /* Bytes of device workspace taco_compress needs for this shape (0 for an
- * invalid shape; the same 20736 bytes for every valid one).  The workspace
- * holds the state of a grid-wide barrier and per-workgroup partial maxima.
+ * invalid shape; the same 37120 bytes for every valid one).  The workspace
+ * holds the state of a grid-wide barrier (call counters and one slot per
+ * workgroup) and per-workgroup partial maxima.
  * It must be zero-filled once when allocated; every call leaves it ready for
  * the next one.  Calls that share a workspace must be ordered (the same
  * stream).  While a single-pass compress runs no other kernel may occupy the

@@ -2,12 +2,16 @@
 modelled step by step on the CPU with random interleavings of the workgroups'
 atomic steps across many calls of varying grid size.
 
-The model follows the protocol described in the kernel source (leaf lines of
-16 workgroups with running counts that advance by exactly 16 per call, a root
-count that advances by 64, padding for partial and unused leaves, leaf maxima
-taken by atomic exchange, release words (call + 1, max)); it checks that every
-workgroup leaves the barrier with the true maximum and that no wait is
-endless.  Host logic only: it does not run the kernel.
+The model follows the protocol described in the kernel source: leaf lines of
+16 workgroups with running counts that advance by exactly 16 per call (each
+workgroup adds 1 to its leaf at its start, the first of a partial leaf also
+the missing arrivals, workgroup 0 advances every leaf the grid does not use),
+so each workgroup's own add yields the call number c; then each workgroup
+stores (c + 1, its max) into its own slot and polls the slots of the grid
+until all carry epoch c + 1.  It checks that every workgroup leaves with the
+true maximum, that no wait is endless, and that calls in which some
+workgroups gave up (bounded waits) leave the state right for the next call.
+Host logic only: it does not run the kernel.
 """
 import random
 
@@ -15,13 +19,13 @@ LEAF, LEAVES = 16, 64
 
 
 def run_calls(seed, calls, spin_limits=(None,)):
-    """spin_limits: per call, a bound on the polls is drawn from this list
-    (None: unbounded).  A workgroup that reaches the bound gives up (NaN, here
-    None) and sets timed_out; it has arrived, so the others still complete."""
+    """spin_limits: per call, a bound on the poll rounds drawn from this list
+    (None: unbounded).  A workgroup that reaches it gives up (NaN, here None)
+    and sets timed_out; it has counted itself and stored its slot."""
     rnd = random.Random(seed)
+    count = [0] * LEAVES
+    slots = {}                                   # workgroup -> (epoch, max)
     timed_out = False
-    leaf = [{"count": 0, "max": 0, "rel": 0} for _ in range(LEAVES)]
-    root = {"count": 0}
     for _ in range(calls):
         G = rnd.choice([1, 2, 15, 16, 17, 100, 255, 256, 512, 1000, 1024])
         nleaves = (G + LEAF - 1) // LEAF
@@ -29,46 +33,35 @@ def run_calls(seed, calls, spin_limits=(None,)):
         limit = rnd.choice(spin_limits)
 
         def workgroup(b):
+            nonlocal timed_out
             l = b // LEAF
             in_leaf = min(LEAF, G - l * LEAF)
-            lf = leaf[l]
-            lf["max"] = max(lf["max"], vals[b])                      # atomic max, waited for
-            yield
             inc = 1 + ((LEAF - in_leaf) if b % LEAF == 0 else 0)
-            lf["count"] += inc                                       # atomic add
-            a = lf["count"]
+            count[l] += inc                                          # atomic add
+            call = (count[l] - 1) // LEAF
             yield
-            call = (a - 1) // LEAF
-            last = False
-            if a % LEAF == 0:
-                rinc = 1 + ((LEAVES - nleaves) if l == 0 else 0)
-                root["count"] += rinc
-                last = root["count"] % LEAVES == 0
-                yield
-            want = (call + 1) & 0xFFFFFFFF
-            if last:
-                mx = 0
-                for k in range(LEAVES):
-                    if k < nleaves:
-                        mx = max(mx, leaf[k]["max"])                 # atomic exchange with 0
-                        leaf[k]["max"] = 0
-                    else:
-                        leaf[k]["count"] = (call + 1) * LEAF
+            if b == 0:
+                for j in range(nleaves, LEAVES):                     # unused leaves
+                    count[j] += LEAF
                     yield
-                for k in range(LEAVES):
-                    leaf[k]["rel"] = (want << 32) | mx
-                    yield
-                return mx
-            spins = 0
-            while (leaf[l]["rel"] >> 32) != want:
-                spins += 1
-                assert spins < 10 ** 6, "endless wait"
-                if limit is not None and spins >= limit:
-                    nonlocal timed_out
+            yield                                                    # loads, rotation
+            slots[b] = (call + 1, vals[b])                           # 64-bit store
+            yield
+            rounds = 0
+            while True:
+                seen = []
+                for j in range(G):                                   # one load per slot
+                    seen.append(slots.get(j, (0, 0)))
+                    if j % 64 == 63:
+                        yield
+                if all(e == call + 1 for e, _ in seen):
+                    return max(v for _, v in seen)
+                rounds += 1
+                assert rounds < 10 ** 5, "endless wait"
+                if limit is not None and rounds >= limit:
                     timed_out = True
                     return None
                 yield
-            return leaf[l]["rel"] & 0xFFFFFFFF
 
         live = {b: workgroup(b) for b in range(G)}
         got = {}
@@ -80,9 +73,10 @@ def run_calls(seed, calls, spin_limits=(None,)):
                 got[b] = e.value
                 del live[b]
         assert all(v is None or v == max(vals) for v in got.values())
-        assert sum(v is not None for v in got.values()) >= 1      # the completing workgroup
         if limit is None:
             assert all(v is not None for v in got.values())
+        assert all(c % LEAF == 0 for c in count)                    # every leaf in step
+        assert len(set(count)) == 1
     return timed_out
 
 

@@ -208,8 +208,8 @@ def _tiles_equal_or_nan(q, ref, block):
 def test_barrier_timeout_gives_nan_codes_and_keeps_the_workspace(taco):
     """The barrier's bounded wait, forced from the host with a bound of one
     poll: the workgroups that give up store NaN codes (never plausible codes
-    under a stale scale), alpha is unaffected, the sticky flag is set, and the
-    workspace stays valid for the next call."""
+    under a stale scale), every other tile is exact, alpha is unaffected, the
+    sticky flag is set, and the workspace stays valid for the next call."""
     block = 128
     x = W.make("gpt3_6p7b_act", seed=4096, tokens=4096).cuda()
     ref = _compress_with(taco, x, block, False, torch.zeros(taco.workspace_bytes(4096, 4096, block),
@@ -223,7 +223,7 @@ def test_barrier_timeout_gives_nan_codes_and_keeps_the_workspace(taco):
         taco.set_barrier_spin_limit(0)
     assert taco.workspace_timed_out(ws)
     eq, nan = _tiles_equal_or_nan(q, ref[0], block)
-    assert eq >= 1 and nan >= 1
+    assert nan >= 1                       # the others may pass or give up too
     assert torch.equal(a, ref[1])
     assert torch.equal(s, ref[2]) or bool(torch.isnan(s).all())
     print("[case] fused compress after the timeout, same workspace", flush=True)
@@ -251,7 +251,7 @@ def test_barrier_timeout_gives_nan_codes_and_keeps_the_workspace(taco):
         taco.set_barrier_spin_limit(0)
     assert taco.workspace_timed_out(ws2)
     eq, nan = _tiles_equal_or_nan(q2, ref2[0], block)
-    assert eq >= 1 and nan >= 1
+    assert nan >= 1                       # the others may pass or give up too
     assert torch.equal(a2, ref2[1])
     for r, t in zip(ref2, taco.decompress_sum_compress(parts, block, workspace=ws2)):
         assert torch.equal(r, t)
