@@ -1608,7 +1608,7 @@ const char* taco_status_string(taco_status_t status) {
   return "TACO_ERR_UNKNOWN";
 }
 
-const char* taco_version(void) { return "0.2.0"; }
+const char* taco_version(void) { return "0.3.0"; }
 
 taco_status_t taco_set_rotation_engine(taco_engine_t engine) {
   // The VALU compress engine has been removed: its kernels took a GPU memory

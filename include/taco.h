@@ -89,7 +89,7 @@ typedef enum {
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* taco_status_string(taco_status_t status);
 
-/* Library version string, e.g. "0.2.0". */
+/* Library version string, e.g. "0.3.0" (0.3: the barrier workspace grew to 37120 bytes). */
 const char* taco_version(void);
 
 /* Select the rotation engine of taco_compress for the whole process (it is
