@@ -77,3 +77,43 @@ def test_gpu_round_trip_has_the_oracles_error():
         zeros_o = np.mean(q_o & 0x7F == 0)
         zeros_g = np.mean(q.cpu().numpy() & 0x7F == 0)
         assert abs(zeros_g - zeros_o) <= 1e-4, name
+
+
+def _kurtosis(v):
+    return float(np.mean(v ** 4) / np.mean(v ** 2) ** 2)
+
+
+def test_rotation_makes_blocks_gaussian_like():
+    """The rotation turns each block's heavy-tailed values into a distribution
+    close to a Gaussian [TACO pt-summary, 2.B.1]: on every synthetic workload
+    the pooled kurtosis of the ASH-scaled blocks is far from 3 (heavy tails)
+    and that of the rotated blocks is at least ten times closer.  For iid
+    Gaussian blocks the rotation is an orthogonal map, so the rotated values
+    stay Gaussian (kurtosis 3 within sampling error)."""
+    for name, tokens, seed in CASES:
+        B = W.WORKLOADS[name].block
+        x = oracle.bf16_bits_to_f64(W.bf16_bits(W.make(name, seed=seed, tokens=tokens))).reshape(-1, B)
+        x = x[np.any(x != 0, axis=1)]
+        a = oracle.ash_scale(oracle.block_energy(x), 1.0)
+        kx = _kurtosis(x * a.astype(np.float64)[:, None])
+        ky = _kurtosis(oracle.hadamard_rotate(x, a))
+        assert abs(ky - 3) * 10 < abs(kx - 3), (name, kx, ky)
+    g = np.random.default_rng(0).standard_normal((4096, 128))
+    bits = oracle.f64_to_bf16_bits(g)
+    xg = oracle.bf16_bits_to_f64(bits)
+    yg = oracle.hadamard_rotate(xg, oracle.ash_scale(oracle.block_energy(xg), 1.0))
+    assert abs(_kurtosis(yg) - 3) < 0.05
+
+
+def test_compressed_volume_is_about_45_percent_smaller():
+    """Codes, block scales and the tensor scale against the bf16 tensor: the
+    ratio is 1/2 + 2/B (+ 4 bytes), a saving of 47-49% per tensor, in line
+    with the average volume reduction the pages report for training
+    [TACO zh-news, results section: about 45% less communication volume]."""
+    for name, tokens, seed in CASES:
+        B = W.WORKLOADS[name].block
+        bits = W.bf16_bits(W.make(name, seed=seed, tokens=tokens))
+        q, a, s = oracle.compress(bits, B)
+        ratio = (q.nbytes + a.nbytes + np.float32(s).nbytes) / bits.nbytes
+        assert ratio == pytest.approx(0.5 + 2 / B + 4 / bits.nbytes, rel=0, abs=1e-12)
+        assert ratio <= 0.55
