@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     get_barrier_spin_limit,
     get_rotation_engine,
     get_single_pass,
+    is_single_pass,
     set_barrier_spin_limit,
     set_rotation_engine,
     set_single_pass,
@@ -36,6 +37,6 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "TACO_AMAX_FLOATS", "TACO_AMAX_SLOTS", "TACO_MAX_PARTS", "TacoError", "compress", "compress_blockscale",
     "compress_delayed", "compress_int8", "decompress", "decompress_blockscale", "decompress_int8", "decompress_sum", "decompress_sum_compress", "get_barrier_spin_limit", "get_rotation_engine",
-    "get_single_pass", "library_path", "load", "num_scales", "set_barrier_spin_limit", "set_rotation_engine", "set_single_pass", "two_shot_allreduce",
+    "get_single_pass", "is_single_pass", "library_path", "load", "num_scales", "set_barrier_spin_limit", "set_rotation_engine", "set_single_pass", "two_shot_allreduce",
     "version", "workspace_bytes", "workspace_timed_out",
 ]

@@ -71,6 +71,8 @@ def load() -> ctypes.CDLL:
         lib.taco_set_single_pass.argtypes = [ctypes.c_int]
         lib.taco_get_single_pass.restype = ctypes.c_int
         lib.taco_get_single_pass.argtypes = []
+        lib.taco_compress_is_single_pass.restype = ctypes.c_int
+        lib.taco_compress_is_single_pass.argtypes = [_i64, _i64, _i32]
         lib.taco_set_barrier_spin_limit.restype = None
         lib.taco_set_barrier_spin_limit.argtypes = [ctypes.c_uint32]
         lib.taco_get_barrier_spin_limit.restype = ctypes.c_uint32
@@ -172,6 +174,14 @@ def set_single_pass(enable: bool) -> None:
     """Fused single-pass compress when the tensor fits on chip (default True);
     False forces the two-kernel path.  Both give identical results."""
     load().taco_set_single_pass(1 if enable else 0)
+
+
+def is_single_pass(tokens: int, hidden: int, block: int) -> bool:
+    """Whether compress of this shape runs as the single fused kernel here."""
+    r = int(load().taco_compress_is_single_pass(tokens, hidden, block))
+    if r < 0:
+        raise ValueError("invalid shape or no usable GPU")
+    return bool(r)
 
 
 def get_single_pass() -> bool:

@@ -1400,30 +1400,45 @@ std::atomic<unsigned> g_spin_limit{kDefaultSpinLimit};   // barrier poll bound (
 
 // Launches the fused compress with TPW tiles per wavefront if every one of its
 // wavefronts can be resident at once (and the barrier has leaves for them).
+// (With launch false it only reports whether the configuration fits.)
 template <int B, int TPW, bool HOLD_Y, int WAVES>
 bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, char* ws,
-               uint4* q, hipStream_t stream) {
+               uint4* q, hipStream_t stream, bool launch) {
   static const int cap = std::min(resident_grid(compress_fused_kernel<B, TPW, HOLD_Y, WAVES>, 64 * WAVES),
                                   kLeaves * kLeafWgs);
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
   if (g > cap) return false;
-  hipLaunchKernelGGL((compress_fused_kernel<B, TPW, HOLD_Y, WAVES>), dim3(g), dim3(64 * WAVES), 0,
-                     stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
+  if (launch)
+    hipLaunchKernelGGL((compress_fused_kernel<B, TPW, HOLD_Y, WAVES>), dim3(g), dim3(64 * WAVES), 0,
+                       stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
   return true;
 }
 
-// Fused configurations, fewest tiles per wavefront first; the rotated blocks
-// take at most 64 of the 128 VGPRs a lane has at 16 wavefronts per CU.
-// Larger tensors (beyond 64 MiB of fp32 y) take the two-pass path.
+// Fused configurations, fewest tiles per wavefront first.  Holding the
+// rotated blocks (fp32 y, at most 64 of the 128 VGPRs a lane has at 16
+// wavefronts per CU) covers 64 MiB of y, e.g. [4096, 4096] at B = 128.
+// Beyond that the wavefronts hold the bf16 input instead (half the registers
+// per element) and rotate it again after the barrier, which covers 1.5 to 2
+// times as much: [8192, 4096] at B = 128 or 256, [8192, 3072] at B = 64.
+// Larger tensors take the two-pass path.  Every variant issues the same
+// MFMA sequence per tile, so all give identical results.
 template <int B>
 bool launch_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, char* ws,
-                  uint4* q, hipStream_t stream) {
-  if (try_fused<B, 1, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream)) return true;
+                  uint4* q, hipStream_t stream, bool launch = true) {
+  if (try_fused<B, 1, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
   if constexpr (B <= 128)
-    if (try_fused<B, 2, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream)) return true;
-  if constexpr (B == 64)
-    if (try_fused<B, 4, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream)) return true;
+    if (try_fused<B, 2, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
+  if constexpr (B == 64) {
+    if (try_fused<B, 4, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
+    if (try_fused<B, 6, false, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
+  }
+  if constexpr (B == 128) {
+    if (try_fused<B, 3, false, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
+    if (try_fused<B, 4, false, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
+  }
+  if constexpr (B == 256)   // 8 wavefronts per CU: 226 VGPRs
+    if (try_fused<B, 4, false, kWavesC / 2>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
   return false;
 }
 
@@ -1625,6 +1640,19 @@ taco_engine_t taco_get_rotation_engine(void) { return static_cast<taco_engine_t>
 void taco_set_single_pass(int enable) { g_single_pass.store(enable != 0); }
 
 int taco_get_single_pass(void) { return g_single_pass.load() ? 1 : 0; }
+
+int taco_compress_is_single_pass(int64_t tokens, int64_t hidden, int32_t block) {
+  if (check_shape(tokens, hidden, block) != TACO_OK || device_cu_count() <= 0) return -1;
+  if (!g_single_pass.load()) return 0;
+  const int64_t nblocks = tokens * (hidden / block);
+  bool fits;
+  switch (block) {
+    case 64: fits = launch_fused<64>(nullptr, nblocks, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, false); break;
+    case 128: fits = launch_fused<128>(nullptr, nblocks, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, false); break;
+    default: fits = launch_fused<256>(nullptr, nblocks, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, false); break;
+  }
+  return fits ? 1 : 0;
+}
 
 void taco_set_barrier_spin_limit(uint32_t polls) {
   g_spin_limit.store(polls == 0 ? kDefaultSpinLimit : polls);

@@ -106,6 +106,14 @@ taco_engine_t taco_get_rotation_engine(void);
 void taco_set_single_pass(int enable);
 int taco_get_single_pass(void);
 
+/* Whether taco_compress of this shape would run as the single fused kernel on
+ * the current device with the current setting: 1 yes, 0 two kernels, -1 for
+ * an invalid shape or no usable device.  The fused kernel holds the rotated
+ * blocks in registers up to 16.8M elements, the bf16 input beyond that, up to
+ * 25.2M elements at block 64 and 33.6M at blocks 128 and 256 on a 256-CU
+ * MI355X; larger tensors take the two kernels. */
+int taco_compress_is_single_pass(int64_t tokens, int64_t hidden, int32_t block);
+
 /* Number of per-block ASH scales of a [tokens, hidden] tensor at this block
  * size (tokens * hidden / block), or -1 if the shape or block is invalid. */
 int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block);

@@ -177,21 +177,28 @@ def test_fused_matches_two_pass_bitwise(taco):
     """The fused kernel and the two-kernel path evaluate the same arithmetic:
     identical codes, alpha and scale.  The shapes alternate between grids of
     many barrier leaves and of one, on one workspace, so every call must find
-    the barrier state the previous call left; the barrier never times out."""
-    nbytes = taco.workspace_bytes(4096, 4096, 128)
+    the barrier state the previous call left; the barrier never times out.
+    Beyond the fused kernel's capacity the library takes two kernels."""
+    nbytes = taco.workspace_bytes(8192, 3584, 128)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    # the last four hold the bf16 input rather than the rotated blocks
+    # (4, 3, 6 and 4 tiles per wavefront; the last with 8 wavefronts per CU)
     cases = [("gpt3_6p7b_act", 4096, 128), ("tiny", 3, 64), ("gpt2_1p5b", 4096, 64),
              ("tiny", 256, 256), ("gpt3_6p7b_grad", 1024, 128), ("dsum_part", 17, 256),
-             ("gpt3_6p7b_act", 4096, 128)]
+             ("gpt3_6p7b_act", 4096, 128), ("qwen_7b", 8192, 128), ("qwen_7b", 5120, 128),
+             ("qwen_7b", 6144, 64), ("qwen_7b", 8192, 256)]
     for name, tokens, block in cases:
         print(f"[case] fused vs two-pass {name} tokens={tokens} block={block}", flush=True)
         x = W.make(name, seed=tokens, tokens=tokens).cuda()
+        assert taco.is_single_pass(*x.shape, block)          # the fused kernel really runs
         fused = _compress_with(taco, x, block, True, ws)
         two = _compress_with(taco, x, block, False, ws)
         for a, b in zip(fused, two):
             assert torch.equal(a, b)
         timed_out = int(ws[8:12].cpu().numpy().view(np.uint32)[0])
         assert timed_out == 0
+    assert not taco.is_single_pass(8192, 3584, 64)            # 29.4M elements at B = 64
+    assert not taco.is_single_pass(16384, 4096, 128)
 
 
 def _tiles_equal_or_nan(q, ref, block):
