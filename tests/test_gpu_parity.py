@@ -471,7 +471,8 @@ def run_delayed(taco, bits, block, E, amax_prev_value):
     return A_o
 
 
-@pytest.mark.parametrize("name,tokens", [("tiny", 3), ("gpt2_1p5b", 37), ("gpt3_6p7b_grad", 21)])
+@pytest.mark.parametrize("name,tokens", [("tiny", 3), ("gpt2_1p5b", 37), ("gpt3_6p7b_grad", 21),
+                                         ("dsum_part", 9)])
 def test_delayed_small_sequence(taco, name, tokens):
     """No history (s = 1), then the first call's maximum (the oracle's, as fp32),
     then a quarter of it (saturation)."""
@@ -480,6 +481,34 @@ def test_delayed_small_sequence(taco, name, tokens):
     A = run_delayed(taco, bits, w.block, 1.0, 0.0)
     run_delayed(taco, bits, w.block, 1.0, float(np.float32(A)))
     run_delayed(taco, bits, w.block, 1.0, float(np.float32(A / 4)))
+
+
+@pytest.mark.parametrize("block", [64, 128, 256])
+def test_dual_scale_variants_edge_cases(taco, block):
+    """Zero tensors, one-hot and constant blocks, and power-of-two magnitudes
+    for the per-block guard and the delayed scale, each against the oracle;
+    scaling x by 2^+-50 must scale alpha by 2^-+50 and leave codes and s_k
+    bitwise unchanged."""
+    H = 4 * block
+    zero = np.zeros((3, H), dtype=np.uint16)
+    run_blockscale(taco, zero, block, 1.0)
+    run_delayed(taco, zero, block, 1.0, 0.0)
+    x = np.zeros((2, H))
+    x[0, 5] = 3.0
+    x[0, block:2 * block] = -0.75
+    x[1, 2 * block + 7] = -2.0 ** -20
+    x[1, 3 * block:] = 1e-3
+    bits = oracle.f64_to_bf16_bits(x)
+    for E in (1.0, 2.0 ** 16):
+        run_blockscale(taco, bits, block, E)
+    run_delayed(taco, bits, block, 1.0, 1.0)
+    base = np.ascontiguousarray(W.bf16_bits(W.make("tiny", seed=2, tokens=4))[:, :H])
+    q0, a0, s0 = run_blockscale(taco, base, block, 1.0)
+    for e in (-50, 50):
+        xs = oracle.f64_to_bf16_bits(oracle.bf16_bits_to_f64(base) * 2.0 ** e)
+        q1, a1, s1 = run_blockscale(taco, xs, block, 1.0)
+        assert np.array_equal(q1, q0) and np.array_equal(s1, s0)
+        assert np.array_equal(a1, (a0.astype(np.float64) * 2.0 ** -e).astype(np.float32))
 
 
 def test_delayed_amax_out_accumulates(taco):
