@@ -594,6 +594,13 @@ def test_graph_replays_match_eager(taco):
         "ds": torch.empty(1, dtype=torch.float32, device=dev),
         "amax": torch.zeros(taco.TACO_AMAX_FLOATS, dtype=torch.float32, device=dev),
         "prev": torch.zeros(taco.TACO_AMAX_FLOATS, dtype=torch.float32, device=dev),
+        "bx": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+        "iq": torch.empty((T, H), dtype=torch.int8, device=dev),
+        "is": torch.empty(1, dtype=torch.float32, device=dev),
+        "ix": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+        "ibq": torch.empty((T, H), dtype=torch.int8, device=dev),
+        "ibs": torch.empty((T, H // B), dtype=torch.float32, device=dev),
+        "ibx": torch.empty((T, H), dtype=torch.bfloat16, device=dev),
     }
     out["prev"][0] = 3.0
 
@@ -605,6 +612,11 @@ def test_graph_replays_match_eager(taco):
         taco.decompress_sum(parts, B, out=out["sum"])
         taco.decompress_sum_compress(parts, B, q=out["rq"], alpha=out["ra"], scale=out["rs"], workspace=ws2)
         taco.compress_blockscale(x2, B, 2.0 ** 12, q=out["bq"], alpha=out["ba"], scale=out["bs"])
+        taco.decompress_blockscale(out["bq"], out["ba"], out["bs"], B, out=out["bx"])
+        taco.compress_int8(x1, 0, q=out["iq"], scale=out["is"], workspace=ws)
+        taco.decompress_int8(out["iq"], out["is"], 0, out=out["ix"])
+        taco.compress_int8(x2, B, q=out["ibq"], scale=out["ibs"])
+        taco.decompress_int8(out["ibq"], out["ibs"], B, out=out["ibx"])
         out["amax"].zero_()
         taco.compress_delayed(x1, B, out["prev"], q=out["dq"], alpha=out["da"], scale=out["ds"],
                               amax_out=out["amax"])
@@ -623,7 +635,7 @@ def test_graph_replays_match_eager(taco):
         ops()
     for rep in range(4):
         for v in out.values():
-            if v.dtype == torch.uint8:
+            if v.dtype in (torch.uint8, torch.int8):
                 v.fill_(0x55)
         g.replay()
         torch.cuda.synchronize()
