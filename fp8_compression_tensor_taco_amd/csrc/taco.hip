@@ -11,25 +11,27 @@
 // [pt-summary 2.A], the inverse [pt-summary 2.B.2], and the local reduction of
 // the two-shot all-reduce [pt-summary 2.B.3].
 //
-// Tiles.  A wavefront works on tiles of 16 consecutive blocks.  Every global
-// access instruction of a wavefront covers whole 64-byte segments: bf16 x is
-// read in the MFMA layout (64 contiguous bytes per block per instruction),
-// FP8 codes and bf16 outputs of decompression move in the quad layout (32
-// and 64 contiguous bytes per quad), and compression codes, which the MFMA
-// layout would scatter in 4-byte pieces, are staged through a padded
-// per-wavefront LDS tile and stored lane-linearly (1 KiB per instruction).
+// Tiles.  A wavefront works on tiles of 16 consecutive blocks.  Global
+// accesses cover whole 64-byte segments or more: bf16 x is read in the MFMA
+// layout (64 contiguous bytes per block per instruction); FP8 codes are read
+// in the wide layout (one 16-byte load per lane, 64 contiguous bytes per
+// quad); compression codes and decompression outputs are staged through a
+// padded per-wavefront LDS tile and stored lane-linearly (1 KiB per
+// instruction); decompress-sum outputs leave from registers after an
+// exchange inside the quad (64 contiguous bytes per quad).
 //
 // Two compute layouts are used for the Walsh-Hadamard rotation of a block:
 //
-// * Quad layout (vector ALUs, decompression).  Four consecutive lanes (a
-//   quad) own one block; lane q holds the elements 32*a + 8*q + b,
-//   a = 0 .. B/32-1, b = 0..7.  The butterflies on element-index bits 0-2 and
-//   5.. are in-lane; bits 3 and 4 cross lanes inside the quad, where a DPP
-//   quad permutation reaches the partner.  That butterfly is computed as
-//   v + c*partner with a per-lane sign c = +-1; lanes whose index bit is set
-//   then hold the negation of their output.  The negation is tracked, not
-//   undone: after both quad stages lane q holds its outputs times
-//   D(q) = c1(q)*c2(q), and D is folded into the scale applied next.
+// * Wide layout (vector ALUs, everything that rotates codes).  Four
+//   consecutive lanes (a quad) own one block; within each 64-element group g,
+//   lane q holds the 16 consecutive elements 64*g + 16*q + (0..15) as two
+//   8-element chunks.  Butterflies on the element-index bits a lane holds
+//   (0-3 and 6..) are in-lane; bits 4 and 5 cross lanes inside the quad,
+//   where a DPP quad permutation reaches the partner.  That butterfly is
+//   computed as v + c*partner with a per-lane sign c = +-1; lanes whose index
+//   bit is set then hold the negation of their output.  The negation is
+//   tracked, not undone: after both quad stages lane q holds its outputs
+//   times D(q) = c1(q)*c2(q), and D is folded into the scale applied next.
 //
 // * MFMA layout (matrix cores, compression).  The rotation of raw x is the
 //   dense product y = H_B x with a +-1 matrix, and x is exactly bf16, so
@@ -37,11 +39,12 @@
 //   See the MFMA section below.
 //
 // Compression needs the tensor-wide max|y| before any code can be written.
-// When the tensor's rotated blocks fit in the registers of the resident
-// wavefronts it is one kernel with a grid-wide barrier (see the fused
-// section); otherwise two kernels over the same tiles: a statistics pass
-// (energy, alpha, rotation, per-workgroup max) and a quantisation pass that
-// folds the workgroup maxima into s, re-reads x and writes the codes.
+// When the tensor fits in the registers of the resident wavefronts (its
+// rotated blocks, or for larger tensors its bf16 input) it is one kernel with
+// a grid-wide barrier (see the fused section); otherwise two kernels over the
+// same tiles: a statistics pass (energy, alpha, rotation, per-workgroup max)
+// and a quantisation pass that folds the workgroup maxima into s, re-reads x
+// and writes the codes.  An INT8 absmax path (no rotation) sits at the end.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -70,7 +73,7 @@ constexpr int kQuadXor2 = 0x4E;         // DPP quad_perm [2,3,0,1]
 
 template <int B>
 struct Blk {
-  static constexpr int NA = B / 32;               // 8-element chunks per lane (quad layout)
+  static constexpr int NA = B / 32;               // 8-element chunks per lane of a quad
   static constexpr int C16 = B / 8;               // 16-byte bf16 chunks per block
   static constexpr float inv_b = 1.0f / B;        // exact (power of two)
   static constexpr float rsqrt_b = B == 64 ? 0.125f
@@ -133,14 +136,6 @@ __device__ __forceinline__ uint4 load16(const uint4* p) {
     return *p;
 }
 
-template <bool NT>
-__device__ __forceinline__ uint2 load8(const uint2* p) {
-  if constexpr (NT)
-    return __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p)));
-  else
-    return *p;
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
@@ -189,40 +184,6 @@ __device__ __forceinline__ void fwht_chunk(float (&v)[8]) {
       }
     }
   }
-}
-
-// Butterflies across the lane's chunks (index bits 5 ..).
-template <int NA>
-__device__ __forceinline__ void fwht_across_chunks(float (&v)[NA][8]) {
-#pragma unroll
-  for (int h = 1; h < NA; h <<= 1) {
-#pragma unroll
-    for (int a = 0; a < NA; a += 2 * h) {
-#pragma unroll
-      for (int c = a; c < a + h; ++c) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = v[c][j], y = v[c + h][j];
-          v[c][j] = x + y;
-          v[c + h][j] = x - y;
-        }
-      }
-    }
-  }
-}
-
-// Butterflies on index bits 3 and 4 (across the quad), with the sign debt
-// described above; c1 = +-1 by quad-lane bit 0, c2 by quad-lane bit 1.
-template <int NA>
-__device__ __forceinline__ void fwht_across_quad(float (&v)[NA][8], float c1, float c2) {
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[a][j] = fmaf(dpp<kQuadXor1>(v[a][j]), c1, v[a][j]);
-#pragma unroll
-  for (int a = 0; a < NA; ++a)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[a][j] = fmaf(dpp<kQuadXor2>(v[a][j]), c2, v[a][j]);
 }
 
 // One butterfly stage on an index bit held across the quad (CTRL: the DPP
@@ -329,7 +290,7 @@ __device__ __forceinline__ int rows_valid(int64_t tile, int64_t nblocks) {
   return r >= kTileBlocks ? kTileBlocks : static_cast<int>(r);
 }
 
-// Lane geometry of the quad layout inside a 16-block tile.
+// Lane geometry of a quad (the four lanes that own one block of a 16-block tile).
 struct Quad {
   int blk;        // block of the tile owned by this lane's quad (0..15)
   int ql;         // position in the quad (0..3)
@@ -757,24 +718,13 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
 
 // ============================================================== decompress
 
-// Hadamard transform of one lane's decoded chunks (bits 0-2, 5.., then 3-4).
-template <int NA>
-__device__ __forceinline__ void rotate_f32(float (&v)[NA][8], const Quad& qd) {
-#pragma unroll
-  for (int a = 0; a < NA; ++a) fwht_chunk<1>(v[a]);
-  fwht_across_chunks<NA>(v);
-  fwht_across_quad<NA>(v, qd.c1, qd.c2);
-}
-
-// The wide layout, used where 16-byte code loads pay (the sums of parts):
-// within each 64-element group g of a block, quad lane ql holds the 16
-// consecutive elements 64 g + 16 ql + (0..15), as chunks 2 g (first 8) and
-// 2 g + 1, so one 16-byte load moves a lane's codes.  Index bits 0-2 lie in a
-// chunk, bit 3 selects the chunk of the pair, bits 4-5 the quad lane and bits
-// 6.. the group.  The butterflies run over the index bits in the order
-// rotate_f32 uses in the quad layout (0-2, 5, 6.., 3, 4), so every value has
-// the magnitude it has there; only the sign of an exact zero can differ,
-// because the sign debt falls on other lanes.
+// Rotation of one block in the wide layout (see the file header): index
+// bits 0-2 lie in a chunk, bit 3 selects the chunk of a pair, bits 4-5 the
+// quad lane and bits 6.. the 64-element group.  The butterflies visit the
+// bits in the order 0-2, 5, 6.., 3, 4.  Any order gives the same transform in
+// exact arithmetic; every kernel that rotates codes uses this one, so their
+// fp32 results agree bitwise (decompress-sum and the fused
+// decompress-sum-compress in particular).
 template <int NA>
 __device__ __forceinline__ void rotate_wide(float (&v)[NA][8], const Quad& qd) {
 #pragma unroll
@@ -847,8 +797,8 @@ constexpr int kOutStride = 2 * B + 32;
 // bf16.  One tile per wavefront per trip, in the wide layout: one 16-byte
 // code load per lane and 64-element group; the bf16 tile goes through the
 // wavefront's LDS image and leaves lane-linearly, 1 KiB of whole cache lines
-// per store instruction (direct stores from the quad layout wrote 64-byte
-// half lines: 11.8 -> 8.9 us on [4096, 4096], B = 128).  SBLK: `scale`
+// per store instruction (direct stores of 64-byte half lines from the
+// registers took 11.8 us instead of 8.9 on [4096, 4096], B = 128).  SBLK: `scale`
 // holds one post-rotation scale per block (the per-block Dual-Scale variant)
 // instead of one per tensor.
 template <int B, bool SBLK>
