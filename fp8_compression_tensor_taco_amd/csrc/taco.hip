@@ -798,10 +798,13 @@ constexpr int kOutStride = 2 * B + 32;
 // code load per lane and 64-element group; the bf16 tile goes through the
 // wavefront's LDS image and leaves lane-linearly, 1 KiB of whole cache lines
 // per store instruction (direct stores of 64-byte half lines from the
-// registers took 11.8 us instead of 8.9 on [4096, 4096], B = 128).  SBLK: `scale`
-// holds one post-rotation scale per block (the per-block Dual-Scale variant)
-// instead of one per tensor.
-template <int B, bool SBLK>
+// registers took 11.8 us instead of 8.9 on [4096, 4096], B = 128).  Each
+// wavefront issues the code loads of U tiles before using any (U = 4 at
+// B = 64, whose 1 KiB tiles are too small to keep the loads in flight
+// otherwise: 10.8 -> 10.2 us; 1 at B = 128 and 256, where more measured
+// slower).  SBLK: `scale` holds one post-rotation scale per block (the
+// per-block Dual-Scale variant) instead of one per tensor.
+template <int B, bool SBLK, int U>
 __global__ __launch_bounds__(kThreads) void decompress_kernel(
     const uint4* __restrict__ q, const float* __restrict__ alpha, const float* __restrict__ scale,
     int64_t nblocks, uint4* __restrict__ out) {
@@ -812,21 +815,31 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
   const float s = SBLK ? 1.0f : *scale;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t < ntiles; t += W) {
-    const int64_t k = t * kTileBlocks + qd.blk;
-    const bool ok = k < nblocks;
-    uint2 raw[NA];
-    load_codes_wide<NA>(q, k, qd.ql, ok, raw);
-    const float al = ok ? alpha[k] : 1.0f;
-    const float sk = SBLK ? (ok ? scale[k] : 1.0f) : s;
-    float v[NA][8];
+  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
+       t0 += W * U) {
+    uint2 raw[U][NA];
+    float al[U], sk[U];
 #pragma unroll
-    for (int a = 0; a < NA; ++a) from_fp8x8(raw[a], v[a]);
-    rotate_wide<NA>(v, qd);
-    wide_tile_to_lds<NA, XS>(v, (Blk<B>::rsqrt_b / (al * sk)) * qd.debt, qd, lds);
-    __builtin_amdgcn_wave_barrier();
-    lds_store_tile_to_global<2 * B, XS, TACO_NT_OUT_STORES != 0>(lds, out, t, rows_valid(t, nblocks));
-    __builtin_amdgcn_wave_barrier();
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = (t0 + u * W) * kTileBlocks + qd.blk;
+      const bool ok = t0 + u * W < ntiles && k < nblocks;
+      load_codes_wide<NA>(q, k, qd.ql, ok, raw[u]);
+      al[u] = ok ? alpha[k] : 1.0f;
+      sk[u] = SBLK ? (ok ? scale[k] : 1.0f) : s;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t t = t0 + u * W;
+      if (t >= ntiles) break;
+      float v[NA][8];
+#pragma unroll
+      for (int a = 0; a < NA; ++a) from_fp8x8(raw[u][a], v[a]);
+      rotate_wide<NA>(v, qd);
+      wide_tile_to_lds<NA, XS>(v, (Blk<B>::rsqrt_b / (al[u] * sk[u])) * qd.debt, qd, lds);
+      __builtin_amdgcn_wave_barrier();
+      lds_store_tile_to_global<2 * B, XS, TACO_NT_OUT_STORES != 0>(lds, out, t, rows_valid(t, nblocks));
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
@@ -1419,8 +1432,9 @@ void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, f
 template <int B, bool SBLK>
 void launch_decompress(const uint8_t* q, const float* alpha, const float* scale, int64_t nblocks,
                        void* out, hipStream_t stream) {
-  hipLaunchKernelGGL((decompress_kernel<B, SBLK>), dim3(tile_grid(nblocks)), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const uint4*>(q), alpha, scale, nblocks, static_cast<uint4*>(out));
+  constexpr int U = B == 64 ? 4 : 1;
+  hipLaunchKernelGGL((decompress_kernel<B, SBLK, U>), dim3((tile_grid(nblocks) + U - 1) / U), dim3(kThreads), 0,
+                     stream, reinterpret_cast<const uint4*>(q), alpha, scale, nblocks, static_cast<uint4*>(out));
 }
 
 template <int B, int P>
