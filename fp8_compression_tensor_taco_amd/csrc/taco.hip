@@ -888,33 +888,57 @@ __device__ __forceinline__ void accumulate_chunks(float (&acc)[NA][8], const uin
 // load per part, all parts' loads issued before any is used, and the bf16
 // result leaves through store_wide_bf16 (staging it through LDS as
 // decompress_kernel does measured slower here: 21.5 -> 24.3 us for 4 parts).
+// At B = 256 with 4, 6 or 8 parts the loads go two parts at a time: all at
+// once took 159-226 VGPRs (2-3 wavefronts per SIMD), two at a time 128
+// (4 wavefronts), 22.8 -> 22.1 us for 4 parts of [4096, 4096]; at B = 64
+// and 128 all parts at once measured fastest.
+template <int B, int P>
+struct DsumChunk {
+  static constexpr int value = (B == 256 && P % 2 == 0 && P > 2) ? 2 : P;
+};
+
 template <int B, int P>
 __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
     Parts parts, int64_t nblocks, uint4* __restrict__ out) {
-  constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16;
+  constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16, PC = DsumChunk<B, P>::value;
   const Quad qd;
-  float s[P];
-#pragma unroll
-  for (int p = 0; p < P; ++p) s[p] = *parts.scale[p];
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t < ntiles; t += W) {
     const int64_t k = t * kTileBlocks + qd.blk;
     const bool ok = k < nblocks;
-    uint2 raw[P][NA];
-    float wt[P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      load_codes_wide<NA>(parts.q[p], k, qd.ql, ok, raw[p]);
-      wt[p] = ok ? parts.alpha[p][k] : 1.0f;
-    }
     float acc[NA][8];
 #pragma unroll
     for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[a][j] = 0.0f;
+    if constexpr (PC == P) {
+      uint2 raw[P][NA];
+      float wt[P];
 #pragma unroll
-    for (int p = 0; p < P; ++p) accumulate_chunks<NA>(acc, raw[p], 1.0f / (wt[p] * s[p]));
+      for (int p = 0; p < P; ++p) {
+        load_codes_wide<NA>(parts.q[p], k, qd.ql, ok, raw[p]);
+        wt[p] = ok ? parts.alpha[p][k] : 1.0f;
+      }
+#pragma unroll
+      for (int p = 0; p < P; ++p) accumulate_chunks<NA>(acc, raw[p], 1.0f / (wt[p] * *parts.scale[p]));
+    } else {
+      // PC parts at a time, in a loop the compiler may not unroll (unrolled,
+      // it hoists every part's loads again and the registers grow back)
+#pragma unroll 1
+      for (int p0 = 0; p0 < P; p0 += PC) {
+        uint2 raw[PC][NA];
+        float wt[PC];
+#pragma unroll
+        for (int j = 0; j < PC; ++j) {
+          load_codes_wide<NA>(pick(parts.q, p0 + j), k, qd.ql, ok, raw[j]);
+          wt[j] = ok ? pick(parts.alpha, p0 + j)[k] : 1.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < PC; ++j)
+          accumulate_chunks<NA>(acc, raw[j], 1.0f / (wt[j] * *pick(parts.scale, p0 + j)));
+      }
+    }
     rotate_wide<NA>(acc, qd);
     store_wide_bf16<NA, TACO_NT_SUM_STORES != 0>(out + k * C16, acc, Blk<B>::rsqrt_b * qd.debt, qd.ql, ok);
   }
@@ -931,8 +955,7 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
 // layout, and continues as compress_fused_kernel (alpha, rotation on the
 // matrix cores, grid-wide max, codes).  The bf16 sum never reaches HBM, and
 // the result is bitwise equal to decompress_sum followed by compress.  The
-// part count is a runtime loop; the next part's codes are loaded before the
-// current part is accumulated.
+// part count is a runtime loop.
 template <int B, int TPW, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     Parts parts, int nparts, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
@@ -964,30 +987,22 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     for (int a = 0; a < NA; ++a)
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[a][j] = 0.0f;
-    uint2 cur[NA], nxt[NA];
-    float wcur, wnxt, scur, snxt;
-    load_codes_wide<NA>(parts.q[0], kq, qd.ql, true, cur);
-    wcur = parts.alpha[0][kq];
-    scur = *parts.scale[0];
+    // One part at a time: loading two or four parts' codes before using
+    // any, or the next part's while accumulating the current one, measured
+    // 3-20% slower ([4096, 4096], B = 64, 128, 256, 2-8 parts).
     for (int p = 0; p < nparts; ++p) {
-      const int pn = p + 1 < nparts ? p + 1 : p;        // the last trip reloads itself
-      load_codes_wide<NA>(pick(parts.q, pn), kq, qd.ql, true, nxt);
-      wnxt = pick(parts.alpha, pn)[kq];
-      snxt = *pick(parts.scale, pn);
+      uint2 raw[NA];
+      load_codes_wide<NA>(pick(parts.q, p), kq, qd.ql, true, raw);
       // (written out here rather than through accumulate_chunks: the call
       // form made the allocator spill at B = 128, TPW = 2)
-      const float wp = 1.0f / (wcur * scur);
+      const float w = 1.0f / (pick(parts.alpha, p)[kq] * *pick(parts.scale, p));
 #pragma unroll
       for (int a = 0; a < NA; ++a) {
         float d[8];
-        from_fp8x8(cur[a], d);
+        from_fp8x8(raw[a], d);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[a][j] = add_product(acc[a][j], d[j], wp);
+        for (int e = 0; e < 8; ++e) acc[a][e] = add_product(acc[a][e], d[e], w);
       }
-#pragma unroll
-      for (int a = 0; a < NA; ++a) cur[a] = nxt[a];
-      wcur = wnxt;
-      scur = snxt;
     }
     rotate_wide<NA>(acc, qd);
     const float r = Blk<B>::rsqrt_b * qd.debt;

@@ -292,7 +292,7 @@ def run_decompress_sum(taco, part_bits, block):
     assert parity.rel_frobenius(got2, ref) <= 1e-3
 
 
-@pytest.mark.parametrize("nparts", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("nparts", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_decompress_sum_small(taco, nparts):
     parts = [W.bf16_bits(W.make("dsum_part", seed=p, tokens=7)) for p in range(nparts)]
     run_decompress_sum(taco, parts, 256)
@@ -380,7 +380,7 @@ def run_decompress_sum_compress(taco, part_bits, block, E=1.0):
     return got
 
 
-@pytest.mark.parametrize("nparts", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("nparts", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_decompress_sum_compress_small(taco, engine, nparts):
     parts = [W.bf16_bits(W.make("dsum_part", seed=p, tokens=7)) for p in range(nparts)]
     run_decompress_sum_compress(taco, parts, 256)
