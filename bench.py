@@ -395,7 +395,7 @@ def main():
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
-            "kernel": ("compress_fused_kernel (single pass)" if taco.get_single_pass()
+            "kernel": ("compress_fused_lds_kernel (single pass)" if taco.get_single_pass()
                        else "compress_stats_mfma_kernel + compress_quant_mfma_kernel"),
             "bound": "hbm",
             "achieved": round(achieved, 1),

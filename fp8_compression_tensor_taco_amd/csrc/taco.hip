@@ -12,8 +12,10 @@
 // the two-shot all-reduce [pt-summary 2.B.3].
 //
 // Tiles.  A wavefront works on tiles of 16 consecutive blocks.  Global
-// accesses cover whole 64-byte segments or more: bf16 x is read in the MFMA
-// layout (64 contiguous bytes per block per instruction); FP8 codes are read
+// accesses cover whole 64-byte segments or more: bf16 x is copied into LDS
+// lane-linearly (1 KiB per instruction) by the fused compress where its tiles
+// fit, and read in the MFMA layout (64 contiguous bytes per block per
+// instruction) elsewhere; FP8 codes are read
 // in the wide layout (one 16-byte load per lane, 64 contiguous bytes per
 // quad); compression codes and decompression outputs are staged through a
 // padded per-wavefront LDS tile and stored lane-linearly (1 KiB per
@@ -105,6 +107,11 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #endif
 #ifndef TACO_NT_OUT_STORES
 #define TACO_NT_OUT_STORES 1
+#endif
+// The fused compress stages x through LDS where its tiles fit (see
+// compress_fused_lds_kernel); 0 selects the direct MFMA-layout loads.
+#ifndef TACO_FUSED_LDS
+#define TACO_FUSED_LDS 1
 #endif
 #ifndef TACO_NT_SUM_STORES
 #define TACO_NT_SUM_STORES 1
@@ -712,6 +719,131 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
     }
     __builtin_amdgcn_wave_barrier();
     lds_store_tile_to_global<B, SROW, TACO_NT_CODE_STORES != 0>(lds, q, t, rows_valid(t, nblocks));
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// The same kernel with x staged through LDS, for the configurations that
+// hold y (a workgroup's tiles then take at most 128 KiB, within gfx950's
+// 160 KiB of LDS per CU).  Each wavefront copies its tiles into its own LDS
+// region with global_load_lds_dwordx4 (16 bytes per lane written straight to
+// LDS at lane-linear positions, 1 KiB per instruction), so every load
+// instruction covers whole cache lines instead of the 64-byte pieces of the
+// direct MFMA-layout loads; the B operand then comes from LDS.  Which global
+// chunk a lane fetches is free as long as each instruction covers its 1 KiB,
+// so chunk k of block n is fetched by the lane that writes position
+// k ^ swz(n) of the block's LDS row: the 16 columns of one K-step then read
+// 16 different 16-byte bank groups.  The arithmetic per tile, and so the
+// result, is that of compress_fused_kernel.
+template <int B>
+struct LdsTile {
+  static constexpr int C16 = B / 8;                        // 16-byte chunks per block
+  static constexpr int kBytes = kTileBlocks * B * 2;       // one bf16 tile
+  static constexpr int kCopies = kBytes / 1024;            // copy instructions per tile
+  // B = 64: a 256-byte LDS row holds two blocks, so the low bit of n picks
+  // the half and the swizzle uses the next three; otherwise the low four.
+  static __device__ __forceinline__ int swz(int n) { return B == 64 ? (n >> 1) & 7 : n & 15; }
+};
+
+// Copies tile t (clamped by the caller) into lds_tile; blocks past the end of
+// the tensor are filled with the tile's last block, as load_tile_mfma does.
+template <int B>
+__device__ __forceinline__ void copy_tile_to_lds(const uint4* __restrict__ x, int64_t t, int64_t nblocks,
+                                                 char* lds_tile) {
+  constexpr int C16 = LdsTile<B>::C16;
+  const int lane = threadIdx.x & 63;
+  const int rv = rows_valid(t, nblocks);
+  const uint4* tile = x + t * (kTileBlocks * C16);
+#pragma unroll
+  for (int d = 0; d < LdsTile<B>::kCopies; ++d) {
+    const int pos = 64 * d + lane;
+    const int n = pos / C16, p = pos % C16;
+    const int row = n < rv ? n : rv - 1;
+    // cache policy 2: non-temporal, as the direct loads (the builtin exists
+    // in the device pass only)
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(tile + row * C16 + (p ^ LdsTile<B>::swz(n)),
+                                     (__attribute__((address_space(3))) void*)(lds_tile + 1024 * d), 16, 0, 2);
+#endif
+  }
+}
+
+template <int B>
+__device__ __forceinline__ void read_tile_from_lds(const char* lds_tile, uint4 (&xr)[B / 32]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int kt = 0; kt < B / 32; ++kt)
+    xr[kt] = *reinterpret_cast<const uint4*>(
+        lds_tile + 16 * (n * LdsTile<B>::C16 + ((4 * kt + g) ^ LdsTile<B>::swz(n))));
+}
+
+template <int B, int TPW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void compress_fused_lds_kernel(
+    const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
+    float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q, unsigned spin_limit) {
+  constexpr int NK = B / 32, NM = B / 16, SROW = Blk<B>::kCodeRowMfma, TB = LdsTile<B>::kBytes;
+  static_assert(WAVES * TPW * TB <= 128 * 1024, "x tiles exceed the LDS budget");
+  static_assert(kTileBlocks * SROW <= TB, "the code tile is staged in the first x tile");
+  __shared__ float red[WAVES];
+  __shared__ float amax_sh;
+  __shared__ __attribute__((aligned(1024))) char xlds_all[WAVES][TPW * TB];
+  char* xlds = xlds_all[threadIdx.x >> 6];
+  const HadFrag F = make_hadamard_fragments();
+  const int lane = threadIdx.x & 63, n = lane & 15;
+  const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + (threadIdx.x >> 6);
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    copy_tile_to_lds<B>(x, t < ntiles ? t : ntiles - 1, nblocks, xlds + i * TB);
+  }
+  // the barrier's call number, counted while the copies are in flight
+  unsigned long long call = 0;
+  if (threadIdx.x < 64) call = count_arrival_wave0(ws);
+  // the copies of this wavefront have landed in LDS (vmcnt(0))
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  f32x4_t y[TPW][NM];
+  float al[TPW];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    const int64_t tc = t < ntiles ? t : ntiles - 1;
+    const int rv = rows_valid(tc, nblocks);
+    uint4 xr[NK];
+    read_tile_from_lds<B>(xlds + i * TB, xr);
+    al[i] = ash_scale(column_sum_squares<B>(xr), sqrt_eb);
+    alpha[tc * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
+    float m = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) {
+      const f32x4_t v = hadamard_mtile<B>(F, xr, mt);
+      y[i][mt] = v;
+      m = fmaxf(fmaxf(m, fabsf(v[0])), fabsf(v[1]));
+      m = fmaxf(fmaxf(m, fabsf(v[2])), fabsf(v[3]));
+    }
+    if (t < ntiles && n < rv) amax = fmaxf(amax, m * (al[i] * Blk<B>::rsqrt_b));
+  }
+  const float wg = workgroup_max<WAVES>(amax, red);
+  if (threadIdx.x < 64) {
+    const float A = grid_max_wave0(wg, call, ws, spin_limit);
+    if (threadIdx.x == 0) amax_sh = A;
+  }
+  __syncthreads();
+  const float A = amax_sh;
+  const float s = A == 0.0f ? 1.0f : kQmax / A;   // NaN stays NaN
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+  // x has been consumed: the first x tile of the wavefront stages its codes
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    if (t >= ntiles) continue;
+    const float c = (al[i] * s) * Blk<B>::rsqrt_b;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) codes_to_lds_mfma<B>(y[i][mt], c, mt, xlds);
+    __builtin_amdgcn_wave_barrier();
+    lds_store_tile_to_global<B, SROW, TACO_NT_CODE_STORES != 0>(xlds, q, t, rows_valid(t, nblocks));
     __builtin_amdgcn_wave_barrier();
   }
 }
@@ -1382,14 +1514,23 @@ std::atomic<unsigned> g_spin_limit{kDefaultSpinLimit};   // barrier poll bound (
 template <int B, int TPW, bool HOLD_Y, int WAVES>
 bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, char* ws,
                uint4* q, hipStream_t stream, bool launch) {
-  static const int cap = std::min(resident_grid(compress_fused_kernel<B, TPW, HOLD_Y, WAVES>, 64 * WAVES),
-                                  kLeaves * kLeafWgs);
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
-  if (g > cap) return false;
-  if (launch)
-    hipLaunchKernelGGL((compress_fused_kernel<B, TPW, HOLD_Y, WAVES>), dim3(g), dim3(64 * WAVES), 0,
-                       stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
+  if constexpr (HOLD_Y && B <= 128 && TACO_FUSED_LDS != 0) {   // these configurations stage x through LDS
+    static const int cap = std::min(resident_grid(compress_fused_lds_kernel<B, TPW, WAVES>, 64 * WAVES),
+                                    kLeaves * kLeafWgs);
+    if (g > cap) return false;
+    if (launch)
+      hipLaunchKernelGGL((compress_fused_lds_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
+                         stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
+  } else {
+    static const int cap = std::min(resident_grid(compress_fused_kernel<B, TPW, HOLD_Y, WAVES>, 64 * WAVES),
+                                    kLeaves * kLeafWgs);
+    if (g > cap) return false;
+    if (launch)
+      hipLaunchKernelGGL((compress_fused_kernel<B, TPW, HOLD_Y, WAVES>), dim3(g), dim3(64 * WAVES), 0,
+                         stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
+  }
   return true;
 }
 
