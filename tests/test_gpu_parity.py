@@ -181,10 +181,13 @@ def test_fused_matches_two_pass_bitwise(taco):
     Beyond the fused kernel's capacity the library takes two kernels."""
     nbytes = taco.workspace_bytes(8192, 3584, 128)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    # the last four hold the bf16 input rather than the rotated blocks
-    # (4, 3, 6 and 4 tiles per wavefront; the last with 8 wavefronts per CU)
+    # B <= 128 holding y: x staged through LDS (1, 2 and 4 tiles per wavefront,
+    # the two 4095-token shapes with a ragged last tile); the last four hold the
+    # bf16 input rather than the rotated blocks (4, 3, 6 and 4 tiles per
+    # wavefront; the last with 8 wavefronts per CU)
     cases = [("gpt3_6p7b_act", 4096, 128), ("tiny", 3, 64), ("gpt2_1p5b", 4096, 64),
              ("tiny", 256, 256), ("gpt3_6p7b_grad", 1024, 128), ("dsum_part", 17, 256),
+             ("qwen_7b", 4096, 64), ("gpt2_1p5b", 4095, 64), ("qwen_7b", 4095, 128),
              ("gpt3_6p7b_act", 4096, 128), ("qwen_7b", 8192, 128), ("qwen_7b", 5120, 128),
              ("qwen_7b", 6144, 64), ("qwen_7b", 8192, 256)]
     for name, tokens, block in cases:
