@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--single-pass", choices=["on", "off"], default="on",
                    help="fused single-pass compress when the tensor fits (default) or the two-kernel path")
+    p.add_argument("--all-configs", action="store_true",
+                   help="also time cold compress and decompress on the other workload shapes "
+                        "(tiny, GPT-2-1.5B, Qwen-7B; reported under 'configs', not the metric)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="before timing, run 8 plain device copies of this many MiB (a known-size "
                         "kernel that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE in the same process)")
@@ -118,6 +121,48 @@ def cpu_baseline(rows: int, min_seconds: float):
             "sample": f"{runs} step(s) on rows 0..{rows - 1} of the [{TOKENS},{HIDDEN}] workload "
                       f"({rows}x{HIDDEN} per tensor; the 4 decompress-sum parts compressed beforehand), "
                       f"numpy fp64, BLAS limited to 1 thread, {dt:.1f} s"}
+
+
+def time_configs(taco, W, dev, stream, capture, time_us):
+    """Cold per-call compress and decompress on the other workload shapes: graphs
+    of back-to-back calls over enough buffer sets to exceed 1 GiB (at most 512)."""
+    import torch
+
+    res = {}
+    for name in ("tiny", "gpt2_1p5b", "qwen_7b"):
+        w = W.WORKLOADS[name]
+        T, H, B = w.tokens, w.hidden, w.block
+        n = T * H
+        x0 = W.make(name, seed=0).to(dev)
+        set_bytes = 2 * n + n + 4 * n // B + 2 * n
+        nsets = min(512, max(4, -(-(1 << 30) // set_bytes)))
+        sets = [{"x": x0.clone(), "q": torch.empty((T, H), dtype=torch.uint8, device=dev),
+                 "a": torch.empty((T, H // B), dtype=torch.float32, device=dev),
+                 "s": torch.empty(1, dtype=torch.float32, device=dev),
+                 "y": torch.empty((T, H), dtype=torch.bfloat16, device=dev)} for _ in range(nsets)]
+        del x0
+        ws = torch.zeros(taco.workspace_bytes(T, H, B), dtype=torch.uint8, device=dev)
+        for st in sets:
+            taco.compress(st["x"], B, q=st["q"], alpha=st["a"], scale=st["s"], workspace=ws)
+        torch.cuda.synchronize()
+        gc = capture(lambda: [taco.compress(st["x"], B, q=st["q"], alpha=st["a"], scale=st["s"], workspace=ws)
+                              for st in sets])
+        gd = capture(lambda: [taco.decompress(st["q"], st["a"], st["s"], B, out=st["y"]) for st in sets])
+        gc.replay()
+        gd.replay()
+        alg = 3 * n + 4 * n // B + 4
+        c_us = time_us(gc.replay, nsets, 4)
+        d_us = time_us(gd.replay, nsets, 4)
+        res[name] = {"shape": [T, H], "block": B, "buffer_sets": nsets,
+                     "single_pass": bool(taco.is_single_pass(T, H, B)),
+                     "compress_us": round(c_us, 3), "decompress_us": round(d_us, 3),
+                     "compress_bf16_GBps": round(2 * n / (c_us * 1e-6) / 1e9, 1),
+                     "decompress_bf16_GBps": round(2 * n / (d_us * 1e-6) / 1e9, 1),
+                     "compress_hbm_frac": round(alg / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "decompress_hbm_frac": round(alg / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del gc, gd, sets, ws
+        torch.cuda.synchronize()
+    return res
 
 
 def main():
@@ -436,6 +481,8 @@ def main():
         "timing": "steps replayed as HIP graphs of one step per buffer set (each step all 5 calls); per-op "
                   f"figures from graphs of back-to-back calls, {OP_PASSES} passes over all buffer sets",
     }
+    if args.all_configs:
+        out["configs"] = time_configs(taco, W, dev, stream, capture, time_us)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_rows, args.cpu_seconds)
     print(json.dumps(out), flush=True)

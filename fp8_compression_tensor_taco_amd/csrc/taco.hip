@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
 // pass the pages describe [TACO pt-summary, 2.B.3].
 //
 // Grid barrier.  The launch makes every workgroup resident at once (grid <=
-// occupancy x CUs).  The only value exchanged is the max, so the barrier is
+// occupancy x CUs, and at most one workgroup per CU).  The only value exchanged is the max, so the barrier is
 // built from device-scope atomic loads, stores and adds alone, with no fences
 // (a device-scope release or acquire would write back or invalidate the whole
 // L2).  Two parts:
@@ -1511,21 +1511,29 @@ std::atomic<unsigned> g_spin_limit{kDefaultSpinLimit};   // barrier poll bound (
 // Launches the fused compress with TPW tiles per wavefront if every one of its
 // wavefronts can be resident at once (and the barrier has leaves for them).
 // (With launch false it only reports whether the configuration fits.)
+// At most one workgroup per CU: at B = 64 with one tile per wavefront two
+// 16-wavefront workgroups fit on a CU, but that grid measured slower than
+// two tiles per wavefront on one workgroup per CU ([4096, 1600]: 400
+// workgroups 9.9 us, 200 workgroups 9.1-9.3 us, 256 workgroups with the
+// tiles spread unevenly 9.4 us, cold).
+int fused_grid_cap(int resident) {
+  const int cus = device_cu_count();
+  return std::min({resident, cus > 0 ? cus : resident, kLeaves * kLeafWgs});
+}
+
 template <int B, int TPW, bool HOLD_Y, int WAVES>
 bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, char* ws,
                uint4* q, hipStream_t stream, bool launch) {
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
   if constexpr (HOLD_Y && B <= 128 && TACO_FUSED_LDS != 0) {   // these configurations stage x through LDS
-    static const int cap = std::min(resident_grid(compress_fused_lds_kernel<B, TPW, WAVES>, 64 * WAVES),
-                                    kLeaves * kLeafWgs);
+    static const int cap = fused_grid_cap(resident_grid(compress_fused_lds_kernel<B, TPW, WAVES>, 64 * WAVES));
     if (g > cap) return false;
     if (launch)
       hipLaunchKernelGGL((compress_fused_lds_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
                          stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
   } else {
-    static const int cap = std::min(resident_grid(compress_fused_kernel<B, TPW, HOLD_Y, WAVES>, 64 * WAVES),
-                                    kLeaves * kLeafWgs);
+    static const int cap = fused_grid_cap(resident_grid(compress_fused_kernel<B, TPW, HOLD_Y, WAVES>, 64 * WAVES));
     if (g > cap) return false;
     if (launch)
       hipLaunchKernelGGL((compress_fused_kernel<B, TPW, HOLD_Y, WAVES>), dim3(g), dim3(64 * WAVES), 0,
