@@ -528,8 +528,9 @@ __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
 // pass the pages describe [TACO pt-summary, 2.B.3].
 //
 // Grid barrier.  The launch makes every workgroup resident at once (grid <=
-// occupancy x CUs, and at most one workgroup per CU).  The only value exchanged is the max, so the barrier is
-// built from device-scope atomic loads, stores and adds alone, with no fences
+// occupancy x CUs, and at most one workgroup per CU).  The only value
+// exchanged is the max, so the barrier is built from device-scope atomic
+// loads, stores and adds alone, with no fences
 // (a device-scope release or acquire would write back or invalidate the whole
 // L2).  Two parts:
 //  * Call number.  Leaf lines of kLeafWgs workgroups each hold a running
