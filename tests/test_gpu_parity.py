@@ -334,6 +334,16 @@ def test_full_size_round_trip(taco, engine, name):
     run_round_trip(taco, bits, w.block)
 
 
+@pytest.mark.parametrize("tokens,block", [(4096, 64), (4095, 128)])
+def test_lds_staged_fused_against_oracle(taco, tokens, block):
+    """The fused compress that copies x into LDS at its larger configurations,
+    element by element against the oracle: [4096, 3584] at B = 64 runs four
+    tiles per wavefront, [4095, 3584] at B = 128 two with a ragged last tile."""
+    assert taco.is_single_pass(tokens, 3584, block)
+    bits = W.bf16_bits(W.make("qwen_7b", seed=7, tokens=tokens))
+    run_round_trip(taco, bits, block)
+
+
 def test_full_size_decompress_sum_32_layers(taco):
     """4 parts of [4096, 4096] at block 256; the same call repeated over 32
     layer slots gives bitwise-identical outputs."""
