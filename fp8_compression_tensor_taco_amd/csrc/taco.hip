@@ -195,12 +195,21 @@ __device__ __forceinline__ void fwht_chunk(float (&v)[8]) {
 
 // One butterfly stage on an index bit held across the quad (CTRL: the DPP
 // quad permutation that pairs the lanes differing in it), with its sign debt c.
-template <int NA, int CTRL>
+// The same quad permutation through the LDS crossbar (ds_swizzle in quad
+// mode): no vector-ALU instruction, for kernels whose vector ALUs are the
+// bottleneck.  The values moved, and so every result, are those of dpp<CTRL>.
+template <int CTRL>
+__device__ __forceinline__ float quad_swizzle(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x8000 | CTRL));
+}
+
+template <int NA, int CTRL, bool SWIZZLE = false>
 __device__ __forceinline__ void fwht_quad_stage(float (&v)[NA][8], float c) {
 #pragma unroll
   for (int a = 0; a < NA; ++a)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[a][j] = fmaf(dpp<CTRL>(v[a][j]), c, v[a][j]);
+    for (int j = 0; j < 8; ++j)
+      v[a][j] = fmaf(SWIZZLE ? quad_swizzle<CTRL>(v[a][j]) : dpp<CTRL>(v[a][j]), c, v[a][j]);
 }
 
 // One butterfly stage on the index bit that selects chunk c or c + H.
@@ -858,15 +867,15 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_lds_kernel(
 // exact arithmetic; every kernel that rotates codes uses this one, so their
 // fp32 results agree bitwise (decompress-sum and the fused
 // decompress-sum-compress in particular).
-template <int NA>
+template <int NA, bool SWIZZLE = false>
 __device__ __forceinline__ void rotate_wide(float (&v)[NA][8], const Quad& qd) {
 #pragma unroll
   for (int a = 0; a < NA; ++a) fwht_chunk<1>(v[a]);
-  fwht_quad_stage<NA, kQuadXor2>(v, qd.c2);           // bit 5
+  fwht_quad_stage<NA, kQuadXor2, SWIZZLE>(v, qd.c2);  // bit 5
   if constexpr (NA >= 4) fwht_chunk_stage<NA, 2>(v);  // bit 6
   if constexpr (NA >= 8) fwht_chunk_stage<NA, 4>(v);  // bit 7
   fwht_chunk_stage<NA, 1>(v);                         // bit 3
-  fwht_quad_stage<NA, kQuadXor1>(v, qd.c1);           // bit 4
+  fwht_quad_stage<NA, kQuadXor1, SWIZZLE>(v, qd.c1);  // bit 4
 }
 
 // One block's codes in the wide layout (a block is 2 NA 16-byte pieces), one
@@ -1137,7 +1146,8 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
         for (int e = 0; e < 8; ++e) acc[a][e] = add_product(acc[a][e], d[e], w);
       }
     }
-    rotate_wide<NA>(acc, qd);
+    // its vector ALUs are its bottleneck: the quad exchanges go through LDS
+    rotate_wide<NA, true>(acc, qd);
     const float r = Blk<B>::rsqrt_b * qd.debt;
     wide_tile_to_lds<NA, XROW>(acc, r, qd, lds);
     __builtin_amdgcn_wave_barrier();
