@@ -17,7 +17,7 @@ Gaussian-like], measured on tensors directly instead of through training:
   taco           ASH + rotation + per-tensor scale (oracle.compress)
 
 Readings: the INT8 rows are oracle/int8.py's quantiser (round half to even,
-clip at +-127, decisions in fp32; the pages give no INT8 details); each FP8
+clip at +-127, exact products; the pages give no INT8 details); each FP8
 ablation keeps the rest of the method unchanged.
 Every function returns the fp64 reconstruction (before any bf16 rounding) and
 the values handed to the rounding step, so that collapse can be measured in
@@ -51,11 +51,11 @@ def quantise(method: str, x_bits: np.ndarray, block: int, target_energy: float =
     if method == "int8_tensor":
         q, sc = i8.compress_int8_tensor(x_bits)
         r = i8.decompress_int8_f64(q, sc, 0)
-        v = (x.astype(np.float32) * sc).astype(np.float64)
+        v = x * np.float64(sc)                       # exact (8- by 24-bit product)
     elif method == "int8_block":
         q, sc = i8.compress_int8_block(x_bits, block)
         r = i8.decompress_int8_f64(q, sc, block)
-        v = (x.astype(np.float32) * np.repeat(sc, block, axis=1)).astype(np.float64)
+        v = x * np.repeat(sc, block, axis=1).astype(np.float64)
     elif method == "fp8_plain":
         r, v = _fp8(xb, _tensor_scale(xb, o.Q_MAX))
     elif method == "fp8_hadamard":

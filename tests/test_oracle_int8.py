@@ -79,22 +79,41 @@ def test_zero_tensor_and_zero_blocks():
     assert not oracle.bf16_bits_to_f64(oracle.decompress_int8(qb, sb, 64))[0, :64].any()
 
 
+def _round_half_even(f: Fraction) -> int:
+    lo = math.floor(f)
+    rem = f - lo
+    return lo + 1 if rem > Fraction(1, 2) else lo if rem < Fraction(1, 2) else lo + (lo & 1)
+
+
+def _nearest_binary(q: Fraction, bits: int) -> Fraction:
+    """The value with `bits` significant bits nearest to q > 0, ties to even
+    (normal range only), by exact rational arithmetic."""
+    e = q.numerator.bit_length() - q.denominator.bit_length()      # 2^e <= q < 2^(e+2)
+    if q < Fraction(2) ** e:
+        e -= 1
+    while q >= Fraction(2) ** (e + 1):
+        e += 1
+    quantum = Fraction(2) ** (e - bits + 1)
+    return _round_half_even(q / quantum) * quantum
+
+
+def _exact_bf16_bits(q: Fraction) -> int:
+    if q == 0:
+        return 0
+    v = _nearest_binary(abs(q), 8)
+    b = int(np.array([float(v)], dtype=np.float32).view(np.uint32)[0] >> 16)   # float(v) exact
+    return b | (0x8000 if q < 0 else 0)
+
+
 def _check_codes_exactly(x_bits, q, s_per_elem):
-    """Every code is the integer nearest to the exact product x * s, except
-    where that product lies within one fp32 rounding of a half-integer (the
-    code is decided on fp32(x * s)); the clamp at +-127 holds."""
+    """Every code is the integer nearest to the exact product x * s (ties to
+    even), clamped to +-127."""
     xs = oracle.bf16_bits_to_f64(x_bits).reshape(-1)
     ss = np.asarray(s_per_elem, dtype=np.float32).reshape(-1)
     for xv, sv, c in zip(xs, ss, q.reshape(-1)):
         p = Fraction(float(xv)) * Fraction(float(sv))
-        lo = math.floor(p)
-        frac = p - lo
-        nearest = lo + 1 if frac > Fraction(1, 2) else lo if frac < Fraction(1, 2) else lo + (lo & 1)
-        nearest = max(-127, min(127, nearest))
-        if abs(frac - Fraction(1, 2)) <= abs(p) * Fraction(1, 2 ** 24):
-            assert c in (max(-127, min(127, lo)), max(-127, min(127, lo + 1)))
-        else:
-            assert c == nearest, (float(xv), float(sv), int(c), nearest)
+        nearest = max(-127, min(127, _round_half_even(p)))
+        assert c == nearest, (float(xv), float(sv), int(c), nearest)
 
 
 def test_codes_against_exact_rational_products():
@@ -109,6 +128,61 @@ def test_codes_against_exact_rational_products():
     assert abs(int(q[i])) == 127
 
 
+def _bf16_values(lo, hi):
+    v = (np.arange(1, 0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    return v[(v >= lo) & (v <= hi)]
+
+
+def test_scale_is_the_correctly_rounded_quotient():
+    """s = fp32(127 / A) is the fp32 value nearest to the exact quotient, for
+    every bf16 A in [2^-20, 2^20] (including those with 127 | m)."""
+    A = _bf16_values(2.0 ** -20, 2.0 ** 20)[::7]
+    s = oracle.int8_scale(A)
+    for a, sv in zip(A, s):
+        assert Fraction(float(sv)) == _nearest_binary(Fraction(127) / Fraction(float(a)), 24), float(a)
+
+
+def test_codes_at_half_way_products_follow_the_exact_product():
+    """x = A/2 gives x * s = 63.5 (1 + d) with d the rounding error of s: an fp32
+    product often lands on 63.5 exactly and would round to 64 (even), while
+    the exact product lies on one side.  Such values decide the code by the
+    exact product."""
+    found = 0
+    for a in _bf16_values(2.0 ** -10, 2.0 ** 10)[::97]:
+        half = np.float32(a) / np.float32(2.0)
+        x = oracle.f64_to_bf16_bits(np.array([[float(a)] + [float(half)] * 63]))
+        q, s = oracle.compress_int8_tensor(x)
+        p32 = float(np.float32(half) * np.float32(s))                 # the fp32 product
+        exact = Fraction(float(half)) * Fraction(float(s))
+        assert int(q[0, 1]) == _round_half_even(exact)
+        if p32 == 63.5 and exact != Fraction(127, 2):
+            found += 1
+            assert int(q[0, 1]) == (63 if exact < Fraction(127, 2) else 64)
+    assert found >= 5            # the case is common, not contrived
+
+
+def test_decode_is_the_correctly_rounded_quotient():
+    """x_hat = bf16(code / s) is the bf16 value nearest to the exact quotient:
+    on pairs where an fp32 reciprocal product or an fp32 division rounds to
+    another bf16 value (found by search), and on a random sample."""
+    rng = np.random.default_rng(3)
+    s = (rng.uniform(0.5, 2.0, 40000) * 2.0 ** rng.integers(-20, 20, 40000)).astype(np.float32)
+    c = np.arange(-127, 128, dtype=np.float32)
+    r = (np.float32(1.0) / s).astype(np.float32)
+    exact64 = c[None, :].astype(np.float64) / s[:, None].astype(np.float64)
+    via_recip = (c[None, :] * r[:, None]).astype(np.float32).astype(np.float64)
+    via_div = (c[None, :] / s[:, None]).astype(np.float32).astype(np.float64)
+    ref = oracle.f64_to_bf16_bits(exact64)
+    hard = np.argwhere((oracle.f64_to_bf16_bits(via_recip) != ref) | (oracle.f64_to_bf16_bits(via_div) != ref))
+    assert len(hard) >= 5
+    sample = np.concatenate([hard, np.stack([rng.integers(0, s.size, 2000), rng.integers(0, c.size, 2000)], 1)])
+    for i, j in sample:
+        q = np.array([[np.int8(c[j])]], dtype=np.int8)
+        got = int(oracle.decompress_int8(q, np.array([s[i]], dtype=np.float32), 0)[0, 0])
+        want = _exact_bf16_bits(Fraction(int(c[j])) / Fraction(float(s[i])))
+        assert got == want, (float(s[i]), int(c[j]), hex(got), hex(want))
+
+
 @pytest.mark.parametrize("block", [0, 64, 256])
 def test_round_trip_error_bound(block):
     rng = np.random.default_rng(7)
@@ -121,8 +195,8 @@ def test_round_trip_error_bound(block):
         se = np.repeat(s, block, axis=1).astype(np.float64)
     xv = oracle.bf16_bits_to_f64(x)
     exact = oracle.decompress_int8_f64(q, s, block)
-    # the code is within 1/2 of fp32(x s), which is within 127 * 2^-24 of x s
-    assert np.all(np.abs(exact - xv) <= 0.5 / se * (1 + 2.0 ** -15))
+    # the code is within 1/2 of the exact product x s (below the clamp)
+    assert np.all(np.abs(exact - xv) <= 0.5 / se * (1 + 2.0 ** -50))
     got = oracle.bf16_bits_to_f64(oracle.decompress_int8(q, s, block))
     assert np.all(np.abs(got - exact) <= 2.0 ** -8 * np.abs(exact) * (1 + 2.0 ** -20))
 
