@@ -13,13 +13,9 @@ from ._binding import (  # noqa: F401
     compress_blockscale,
     compress_delayed,
     compress_int8,
-    get_barrier_spin_limit,
-    get_rotation_engine,
-    get_single_pass,
+    TACO_DEFAULT_BARRIER_POLLS,
+    TACO_FLAG_TWO_PASS,
     is_single_pass,
-    set_barrier_spin_limit,
-    set_rotation_engine,
-    set_single_pass,
     two_shot_allreduce,
     decompress,
     decompress_blockscale,
@@ -35,8 +31,9 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "TACO_AMAX_FLOATS", "TACO_AMAX_SLOTS", "TACO_MAX_PARTS", "TacoError", "compress", "compress_blockscale",
-    "compress_delayed", "compress_int8", "decompress", "decompress_blockscale", "decompress_int8", "decompress_sum", "decompress_sum_compress", "get_barrier_spin_limit", "get_rotation_engine",
-    "get_single_pass", "is_single_pass", "library_path", "load", "num_scales", "set_barrier_spin_limit", "set_rotation_engine", "set_single_pass", "two_shot_allreduce",
-    "version", "workspace_bytes", "workspace_timed_out",
+    "TACO_AMAX_FLOATS", "TACO_AMAX_SLOTS", "TACO_DEFAULT_BARRIER_POLLS", "TACO_FLAG_TWO_PASS", "TACO_MAX_PARTS",
+    "TacoError", "compress", "compress_blockscale", "compress_delayed", "compress_int8", "decompress",
+    "decompress_blockscale", "decompress_int8", "decompress_sum", "decompress_sum_compress", "is_single_pass",
+    "library_path", "load", "num_scales", "two_shot_allreduce", "version", "workspace_bytes",
+    "workspace_timed_out",
 ]

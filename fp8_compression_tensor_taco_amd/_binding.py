@@ -7,6 +7,7 @@ tensors that are not on a GPU, every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -21,9 +22,10 @@ TACO_AMAX_FLOATS = 4096
 _STATUS = {
     0: "TACO_OK", 1: "TACO_ERR_NULL", 2: "TACO_ERR_ALIGN", 3: "TACO_ERR_SHAPE",
     4: "TACO_ERR_UNSUPPORTED_BLOCK", 5: "TACO_ERR_BAD_ENERGY", 6: "TACO_ERR_WORKSPACE",
-    7: "TACO_ERR_BAD_NPARTS", 8: "TACO_ERR_HIP", 9: "TACO_ERR_BAD_ENGINE", 10: "TACO_ERR_ALIAS",
+    7: "TACO_ERR_BAD_NPARTS", 8: "TACO_ERR_HIP", 9: "TACO_ERR_FLAGS", 10: "TACO_ERR_ALIAS",
 }
-ENGINES = {"auto": 0, "valu": 1, "mfma": 2}
+TACO_FLAG_TWO_PASS = 1
+TACO_DEFAULT_BARRIER_POLLS = 1 << 16
 
 
 class TacoError(RuntimeError):
@@ -42,6 +44,7 @@ _workspaces: dict[tuple[int, str, int], torch.Tensor] = {}
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
+_u32 = ctypes.c_uint32
 
 
 def library_path() -> str:
@@ -63,20 +66,8 @@ def load() -> ctypes.CDLL:
         lib.taco_status_string.argtypes = [ctypes.c_int]
         lib.taco_version.restype = ctypes.c_char_p
         lib.taco_version.argtypes = []
-        lib.taco_set_rotation_engine.restype = ctypes.c_int
-        lib.taco_set_rotation_engine.argtypes = [ctypes.c_int]
-        lib.taco_get_rotation_engine.restype = ctypes.c_int
-        lib.taco_get_rotation_engine.argtypes = []
-        lib.taco_set_single_pass.restype = None
-        lib.taco_set_single_pass.argtypes = [ctypes.c_int]
-        lib.taco_get_single_pass.restype = ctypes.c_int
-        lib.taco_get_single_pass.argtypes = []
         lib.taco_compress_is_single_pass.restype = ctypes.c_int
         lib.taco_compress_is_single_pass.argtypes = [_i64, _i64, _i32]
-        lib.taco_set_barrier_spin_limit.restype = None
-        lib.taco_set_barrier_spin_limit.argtypes = [ctypes.c_uint32]
-        lib.taco_get_barrier_spin_limit.restype = ctypes.c_uint32
-        lib.taco_get_barrier_spin_limit.argtypes = []
         lib.taco_workspace_timed_out.restype = ctypes.c_int
         lib.taco_workspace_timed_out.argtypes = [_vp, _vp, ctypes.POINTER(ctypes.c_int)]
         lib.taco_num_scales.restype = _i64
@@ -86,6 +77,9 @@ def load() -> ctypes.CDLL:
         lib.taco_compress.restype = ctypes.c_int
         lib.taco_compress.argtypes = [_vp, _i64, _i64, _i32, ctypes.c_float, _vp, _vp, _vp,
                                       _vp, ctypes.c_size_t, _vp]
+        lib.taco_compress_ex.restype = ctypes.c_int
+        lib.taco_compress_ex.argtypes = [_vp, _i64, _i64, _i32, ctypes.c_float, _vp, _vp, _vp,
+                                         _vp, ctypes.c_size_t, _u32, _u32, _vp]
         lib.taco_decompress.restype = ctypes.c_int
         lib.taco_decompress.argtypes = [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
         lib.taco_decompress_sum_compress_workspace_bytes.restype = ctypes.c_size_t
@@ -95,6 +89,11 @@ def load() -> ctypes.CDLL:
                                                      ctypes.POINTER(_vp), _i32, _i64, _i64, _i32,
                                                      ctypes.c_float, _vp, _vp, _vp, _vp,
                                                      ctypes.c_size_t, _vp]
+        lib.taco_decompress_sum_compress_ex.restype = ctypes.c_int
+        lib.taco_decompress_sum_compress_ex.argtypes = [ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                                        ctypes.POINTER(_vp), _i32, _i64, _i64, _i32,
+                                                        ctypes.c_float, _vp, _vp, _vp, _vp,
+                                                        ctypes.c_size_t, _u32, _u32, _vp]
         lib.taco_compress_blockscale.restype = ctypes.c_int
         lib.taco_compress_blockscale.argtypes = [_vp, _i64, _i64, _i32, ctypes.c_float, _vp, _vp, _vp, _vp]
         lib.taco_decompress_blockscale.restype = ctypes.c_int
@@ -131,6 +130,17 @@ def _stream(device: torch.device, stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on(stream):
+    """Allocations (outputs and .contiguous() copies) on the stream the call
+    runs on, so that torch's caching allocator does not hand their memory to
+    another stream while the call's kernels still use it."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
+
+
 def _require_buffer(t: torch.Tensor, name: str, dtype, numel: int, shape=None) -> None:
     """Output / input buffers must be contiguous, of the right dtype and size:
     the kernels index them by the shape alone."""
@@ -158,24 +168,6 @@ def version() -> str:
     return load().taco_version().decode()
 
 
-def set_rotation_engine(name: str) -> None:
-    """Rotation engine of compress for this process: "auto", "valu" or "mfma"."""
-    if name not in ENGINES:
-        raise ValueError(f"unknown engine {name!r}; expected one of {sorted(ENGINES)}")
-    _check(load().taco_set_rotation_engine(ENGINES[name]))
-
-
-def get_rotation_engine() -> str:
-    v = load().taco_get_rotation_engine()
-    return {i: n for n, i in ENGINES.items()}[v]
-
-
-def set_single_pass(enable: bool) -> None:
-    """Fused single-pass compress when the tensor fits on chip (default True);
-    False forces the two-kernel path.  Both give identical results."""
-    load().taco_set_single_pass(1 if enable else 0)
-
-
 def is_single_pass(tokens: int, hidden: int, block: int) -> bool:
     """Whether compress of this shape runs as the single fused kernel here."""
     r = int(load().taco_compress_is_single_pass(tokens, hidden, block))
@@ -184,21 +176,18 @@ def is_single_pass(tokens: int, hidden: int, block: int) -> bool:
     return bool(r)
 
 
-def get_single_pass() -> bool:
-    return bool(load().taco_get_single_pass())
+def _pass_args(single_pass: bool, barrier_polls: int):
+    if not 0 <= int(barrier_polls) < 2 ** 32:
+        raise ValueError("barrier_polls must fit in 32 bits")
+    return (0 if single_pass else TACO_FLAG_TWO_PASS), int(barrier_polls)
 
 
-def set_barrier_spin_limit(polls: int) -> None:
-    """Bound on the grid barrier's polls in the single-pass kernels (0: the
-    default, 2^22).  A workgroup that gives up stores NaN codes and sets the
-    workspace's timeout flag; every kernel still finishes."""
-    if not 0 <= int(polls) < 2 ** 32:
-        raise ValueError("polls must fit in 32 bits")
-    load().taco_set_barrier_spin_limit(int(polls))
-
-
-def get_barrier_spin_limit() -> int:
-    return int(load().taco_get_barrier_spin_limit())
+def _timed_out_and_clear(lib, workspace: torch.Tensor, handle: int) -> bool:
+    flag = ctypes.c_int(0)
+    _check(lib.taco_workspace_timed_out(_ptr(workspace), handle, ctypes.byref(flag)))
+    if flag.value:
+        workspace.zero_()
+    return bool(flag.value)
 
 
 def workspace_timed_out(workspace: torch.Tensor | None = None, stream=None) -> bool:
@@ -247,16 +236,32 @@ def _workspace(device: torch.device, nbytes: int, kind: str, stream_handle: int)
 def compress(x: torch.Tensor, block: int, target_energy: float = 1.0, *,
              q: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
              scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-             stream=None):
+             stream=None, single_pass: bool = True, barrier_polls: int = 0,
+             check_barrier: bool = False):
     """Compress a bf16 [tokens, hidden] GPU tensor.
 
     Returns (q uint8 [tokens, hidden], alpha float32 [tokens, hidden/block],
     scale float32 [1]).  Output tensors may be passed in to avoid allocation.
+    single_pass=False takes the two kernels that need no co-residency (for
+    callers whose compute units are shared with other kernels; the same
+    result bitwise).  barrier_polls bounds the single-pass barrier's wait (0:
+    the library's default).  check_barrier=True waits for the call and, if a
+    workgroup gave up at the barrier, clears the workspace's flag and
+    compresses again with the two kernels (the fallback include/taco.h
+    documents); it synchronises the stream.
     """
+    with _on(stream):
+        return _compress(x, block, target_energy, q, alpha, scale, workspace, stream, single_pass,
+                         barrier_polls, check_barrier)
+
+
+def _compress(x, block, target_energy, q, alpha, scale, workspace, stream, single_pass, barrier_polls,
+              check_barrier):
     lib = load()
     if x.dim() != 2 or x.dtype != torch.bfloat16:
         raise ValueError("x must be a 2-D bfloat16 tensor")
     dev = _require_gpu(x)
+    flags, polls = _pass_args(single_pass, barrier_polls)
     x = x.contiguous()
     T, H = x.shape
     n = lib.taco_num_scales(T, H, block)
@@ -277,15 +282,23 @@ def compress(x: torch.Tensor, block: int, target_energy: float = 1.0, *,
     _require_buffer(scale, "scale", torch.float32, 1)
     if not workspace.is_contiguous():
         raise ValueError("workspace must be contiguous")
-    _check(lib.taco_compress(_ptr(x), T, H, block, float(target_energy), _ptr(q), _ptr(alpha),
-                             _ptr(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                             _stream(dev, stream)))
+    args = (_ptr(x), T, H, block, float(target_energy), _ptr(q), _ptr(alpha), _ptr(scale), _ptr(workspace),
+            workspace.numel() * workspace.element_size())
+    handle = _stream(dev, stream)
+    _check(lib.taco_compress_ex(*args, flags, polls, handle))
+    if check_barrier and flags == 0 and _timed_out_and_clear(lib, workspace, handle):
+        _check(lib.taco_compress_ex(*args, TACO_FLAG_TWO_PASS, polls, handle))
     return q, alpha, scale
 
 
 def decompress(q: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, block: int, *,
                out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Decompress (q, alpha, scale) into a bf16 [tokens, hidden] GPU tensor."""
+    with _on(stream):
+        return _decompress(q, alpha, scale, block, out, stream)
+
+
+def _decompress(q, alpha, scale, block, out, stream):
     lib = load()
     if q.dim() != 2 or q.dtype != torch.uint8:
         raise ValueError("q must be a 2-D uint8 tensor")
@@ -317,10 +330,20 @@ def _check_parts(lib, parts):
 def decompress_sum_compress(parts, block: int, target_energy: float = 1.0, *,
                             q: torch.Tensor | None = None, alpha: torch.Tensor | None = None,
                             scale: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-                            stream=None):
+                            stream=None, single_pass: bool = True, barrier_polls: int = 0,
+                            check_barrier: bool = False):
     """compress(decompress_sum(parts)) in one call: returns (q, alpha, scale) of
-    the bf16 sum of the parts' reconstructions."""
+    the bf16 sum of the parts' reconstructions.  single_pass, barrier_polls
+    and check_barrier as in compress()."""
+    with _on(stream):
+        return _decompress_sum_compress(parts, block, target_energy, q, alpha, scale, workspace, stream,
+                                        single_pass, barrier_polls, check_barrier)
+
+
+def _decompress_sum_compress(parts, block, target_energy, q, alpha, scale, workspace, stream, single_pass,
+                             barrier_polls, check_barrier):
     lib = load()
+    flags, polls = _pass_args(single_pass, barrier_polls)
     parts, dev = _check_parts(lib, parts)
     T, H = parts[0][0].shape
     for pq, pa, ps in parts:
@@ -354,16 +377,23 @@ def decompress_sum_compress(parts, block: int, target_energy: float = 1.0, *,
     qa = (_vp * P)(*[p[0].data_ptr() for p in parts])
     aa = (_vp * P)(*[p[1].data_ptr() for p in parts])
     sa = (_vp * P)(*[p[2].data_ptr() for p in parts])
-    _check(lib.taco_decompress_sum_compress(qa, aa, sa, P, T, H, block, float(target_energy),
-                                            _ptr(q), _ptr(alpha), _ptr(scale), _ptr(workspace),
-                                            workspace.numel() * workspace.element_size(),
-                                            _stream(dev, stream)))
+    args = (qa, aa, sa, P, T, H, block, float(target_energy), _ptr(q), _ptr(alpha), _ptr(scale),
+            _ptr(workspace), workspace.numel() * workspace.element_size())
+    handle = _stream(dev, stream)
+    _check(lib.taco_decompress_sum_compress_ex(*args, flags, polls, handle))
+    if check_barrier and flags == 0 and _timed_out_and_clear(lib, workspace, handle):
+        _check(lib.taco_decompress_sum_compress_ex(*args, TACO_FLAG_TWO_PASS, polls, handle))
     return q, alpha, scale
 
 
 def decompress_sum(parts, block: int, *, out: torch.Tensor | None = None,
                    stream=None) -> torch.Tensor:
     """Sum of the decompressions of ``parts`` (a list of (q, alpha, scale)), rounded once to bf16."""
+    with _on(stream):
+        return _decompress_sum(parts, block, out, stream)
+
+
+def _decompress_sum(parts, block, out, stream):
     lib = load()
     parts = [(q.contiguous(), a.contiguous(), s) for q, a, s in parts]
     if not 1 <= len(parts) <= TACO_MAX_PARTS:
@@ -383,9 +413,6 @@ def decompress_sum(parts, block: int, *, out: torch.Tensor | None = None,
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     _require_gpu(parts[0][0], out)
     _require_buffer(out, "out", torch.bfloat16, T * H, (T, H))
-    for q, _, _ in parts:
-        if q.data_ptr() == out.data_ptr():
-            raise ValueError("out may not alias an input")
     P = len(parts)
     qa = (_vp * P)(*[q.data_ptr() for q, _, _ in parts])
     aa = (_vp * P)(*[a.data_ptr() for _, a, _ in parts])
@@ -421,16 +448,22 @@ def compress_blockscale(x: torch.Tensor, block: int, target_energy: float = 1.0,
                         scale: torch.Tensor | None = None, stream=None):
     """Dual-Scale variant with a per-block overflow guard: returns (q, alpha,
     scale [tokens, hidden/block]); one streaming kernel."""
-    x = x.contiguous()
-    lib, dev, T, H, q, alpha, scale = _compress_outputs(x, block, q, alpha, scale, True)
-    _check(lib.taco_compress_blockscale(_ptr(x), T, H, block, float(target_energy), _ptr(q), _ptr(alpha),
-                                        _ptr(scale), _stream(dev, stream)))
-    return q, alpha, scale
+    with _on(stream):
+        x = x.contiguous()
+        lib, dev, T, H, q, alpha, scale = _compress_outputs(x, block, q, alpha, scale, True)
+        _check(lib.taco_compress_blockscale(_ptr(x), T, H, block, float(target_energy), _ptr(q), _ptr(alpha),
+                                            _ptr(scale), _stream(dev, stream)))
+        return q, alpha, scale
 
 
 def decompress_blockscale(q: torch.Tensor, alpha: torch.Tensor, scale: torch.Tensor, block: int, *,
                           out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Inverse of compress_blockscale (one post-rotation scale per block)."""
+    with _on(stream):
+        return _decompress_blockscale(q, alpha, scale, block, out, stream)
+
+
+def _decompress_blockscale(q, alpha, scale, block, out, stream):
     lib = load()
     if q.dim() != 2 or q.dtype != torch.uint8:
         raise ValueError("q must be a 2-D uint8 tensor")
@@ -465,6 +498,11 @@ def compress_int8(x: torch.Tensor, block: int = 0, *, q: torch.Tensor | None = N
     """INT8 degrade path: symmetric absmax INT8 of a bf16 [tokens, hidden] GPU
     tensor, one scale per tensor (block 0) or per block of `block` elements.
     Returns (q int8 [tokens, hidden], scale float32 [1] or [tokens, hidden/block])."""
+    with _on(stream):
+        return _compress_int8(x, block, q, scale, workspace, stream)
+
+
+def _compress_int8(x, block, q, scale, workspace, stream):
     lib = load()
     if x.dim() != 2 or x.dtype != torch.bfloat16:
         raise ValueError("x must be a 2-D bfloat16 tensor")
@@ -496,6 +534,11 @@ def compress_int8(x: torch.Tensor, block: int = 0, *, q: torch.Tensor | None = N
 def decompress_int8(q: torch.Tensor, scale: torch.Tensor, block: int = 0, *,
                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Inverse of compress_int8 with the same block: bf16 [tokens, hidden]."""
+    with _on(stream):
+        return _decompress_int8(q, scale, block, out, stream)
+
+
+def _decompress_int8(q, scale, block, out, stream):
     lib = load()
     if q.dim() != 2 or q.dtype != torch.int8:
         raise ValueError("q must be a 2-D int8 tensor")
@@ -524,6 +567,11 @@ def compress_delayed(x: torch.Tensor, block: int, amax_prev: torch.Tensor | None
     this tensor's largest |y| as its maximum (TACO_AMAX_FLOATS fp32; see
     include/taco.h), to pass as amax_prev next time.
     Decompress with decompress()."""
+    with _on(stream):
+        return _compress_delayed(x, block, amax_prev, target_energy, q, alpha, scale, amax_out, stream)
+
+
+def _compress_delayed(x, block, amax_prev, target_energy, q, alpha, scale, amax_out, stream):
     x = x.contiguous()
     lib, dev, T, H, q, alpha, scale = _compress_outputs(x, block, q, alpha, scale, False)
     if amax_prev is None:
@@ -538,25 +586,28 @@ def compress_delayed(x: torch.Tensor, block: int, amax_prev: torch.Tensor | None
     return q, alpha, scale, amax_out
 
 
-def two_shot_allreduce(xs, block: int, target_energy: float = 1.0, stream=None) -> torch.Tensor:
+def two_shot_allreduce(xs, block: int, target_energy: float = 1.0, stream=None,
+                       single_pass: bool = True) -> torch.Tensor:
     """The compressed two-shot all-reduce of P bf16 [T, H] tensors as P ranks
     would run it, emulated on one GPU with the library's calls: each rank's
     compress; per row shard j (T/P whole rows), decompress_sum_compress over
     the ranks' rows of that shard (the reduce-scatter step, FP8 out for the
-    all-gather); decompress of every reduced shard.  Returns the bf16 result."""
-    xs = [x.contiguous() for x in xs]
-    P = len(xs)
-    if P < 1 or P > TACO_MAX_PARTS:
-        _check(7)
-    T, H = xs[0].shape
-    if T % P != 0 or any(x.shape != (T, H) for x in xs):
-        raise ValueError("P tensors of one shape whose rows split into P equal shards")
-    rows = T // P
-    comp = [compress(x, block, target_energy, stream=stream) for x in xs]
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=xs[0].device)
-    for j in range(P):
-        sl = slice(j * rows, (j + 1) * rows)
-        red = decompress_sum_compress([(q[sl], a[sl], s) for q, a, s in comp], block, target_energy,
-                                      stream=stream)
-        decompress(*red, block, out=out[sl], stream=stream)
-    return out
+    all-gather); decompress of every reduced shard.  Returns the bf16 result.
+    single_pass as in compress()."""
+    with _on(stream):
+        xs = [x.contiguous() for x in xs]
+        P = len(xs)
+        if P < 1 or P > TACO_MAX_PARTS:
+            _check(7)
+        T, H = xs[0].shape
+        if T % P != 0 or any(x.shape != (T, H) for x in xs):
+            raise ValueError("P tensors of one shape whose rows split into P equal shards")
+        rows = T // P
+        comp = [compress(x, block, target_energy, stream=stream, single_pass=single_pass) for x in xs]
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=xs[0].device)
+        for j in range(P):
+            sl = slice(j * rows, (j + 1) * rows)
+            red = decompress_sum_compress([(q[sl], a[sl], s) for q, a, s in comp], block, target_energy,
+                                          stream=stream, single_pass=single_pass)
+            decompress(*red, block, out=out[sl], stream=stream)
+        return out

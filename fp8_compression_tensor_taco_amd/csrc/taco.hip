@@ -53,8 +53,8 @@
 #include <stdint.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cstddef>
+#include <initializer_list>
 
 #include "taco.h"
 
@@ -559,12 +559,17 @@ __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
 //    beyond this grid are never read; a slot can only hold epoch c + 1 if it
 //    was written in this call, since epochs only grow (zero-filling the
 //    workspace resets counts and slots together).
-// The poll is bounded (spin_limit polls, set by the host): a workgroup that
-// gives up sets the sticky timed_out flag and takes NaN as the max, so its
-// codes are all E4M3 NaN rather than plausible values under a stale scale.
-// It has already counted itself and stored its slot, so the barrier still
-// completes for the others and the workspace stays consistent for the next
-// call; every wavefront finishes.
+// Epochs are the low 32 bits of the call number, and a slot left from long
+// ago could carry the current epoch after 2^32 calls.  So workgroup 0 also
+// writes the current epoch into every slot beyond this grid: after any call
+// every one of the kMaxSlots slots holds that call's epoch, and the next call
+// waits for the next epoch, which differs from it whatever the grid sizes.
+// The poll is bounded (spin_limit polls, chosen per call by the host): a
+// workgroup that gives up sets the sticky timed_out flag and takes NaN as the
+// max, so its codes are all E4M3 NaN rather than plausible values under a
+// stale scale.  It has already counted itself and stored its slot, so the
+// barrier still completes for the others and the workspace stays consistent
+// for the next call; every wavefront finishes.
 
 constexpr int kLine = 256;               // bytes per leaf line
 constexpr int kLeafWgs = 16;             // workgroups per leaf
@@ -572,7 +577,8 @@ constexpr int kLeaves = 64;              // leaf lines => at most 1024 fused wor
 constexpr size_t kPartialOffset = static_cast<size_t>(kLine) * (1 + kLeaves);
 constexpr size_t kSlotOffset = kPartialOffset + kMaxPartials * sizeof(float);
 constexpr int kSlotStride = 16;          // bytes per workgroup slot
-constexpr unsigned kDefaultSpinLimit = 1u << 22;
+constexpr int kMaxSlots = kLeaves * kLeafWgs;
+constexpr unsigned kDefaultSpinLimit = TACO_DEFAULT_BARRIER_POLLS;
 
 struct RootLine {
   unsigned long long unused;
@@ -606,36 +612,45 @@ __device__ __forceinline__ T add_agent(T* p, T v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The call number of this launch on this workspace; called by the 64 lanes
-// of wavefront 0 (lane 0 counts this workgroup into its leaf; in workgroup 0,
-// lane l >= the grid's leaf count advances leaf l).  Only lane 0's value is
-// meaningful; grid_max_wave0 broadcasts it.
-__device__ __forceinline__ unsigned long long count_arrival_wave0(char* __restrict__ ws) {
+// Counts this workgroup into its leaf; called by the 64 lanes of wavefront 0
+// (lane 0 adds this workgroup's arrivals; in workgroup 0, lane l >= the grid's
+// leaf count advances leaf l).  The adds return nothing; then every lane loads
+// its workgroup's leaf count, with no branch around the load, so that nothing
+// waits for it before the barrier needs it.  That count lies in
+// [16 c + 1, 16 c + 16] for call number c: this workgroup's own add precedes
+// the load in the lane's program order on the same word, every leaf stood at
+// 16 c when the call began, and the call adds exactly 16.
+__device__ __forceinline__ unsigned long long arrive_wave0(char* __restrict__ ws) {
   const int lane = threadIdx.x & 63;
   const unsigned l = blockIdx.x / kLeafWgs;
   const unsigned nleaves = (gridDim.x + kLeafWgs - 1) / kLeafWgs;
-  unsigned long long call = 0;
   if (lane == 0) {
     const unsigned in_leaf = min(static_cast<unsigned>(kLeafWgs), gridDim.x - l * kLeafWgs);
     unsigned long long inc = 1;
     if (blockIdx.x % kLeafWgs == 0) inc += kLeafWgs - in_leaf;
-    call = (add_agent(&leaf_line(ws, l)->count, inc) + inc - 1) / kLeafWgs;
+    add_agent(&leaf_line(ws, l)->count, inc);
   } else if (blockIdx.x == 0 && static_cast<unsigned>(lane) >= nleaves) {
     add_agent(&leaf_line(ws, lane)->count, static_cast<unsigned long long>(kLeafWgs));
   }
-  return call;
+  return load_agent(&leaf_line(ws, l)->count);
 }
-static_assert(kLeaves == 64, "count_arrival_wave0 advances one unused leaf per lane");
+static_assert(kLeaves == 64, "arrive_wave0 advances one unused leaf per lane");
 
 // Grid-wide max; called by the 64 lanes of wavefront 0 with the workgroup's
-// max (uniform) and lane 0's call number.  Every lane returns the tensor-wide
-// max, or NaN if this workgroup gave up waiting.
-__device__ float grid_max_wave0(float wg_max, unsigned long long call, char* __restrict__ ws,
+// max (uniform) and the leaf count arrive_wave0 returned.  Every lane returns
+// the tensor-wide max, or NaN if this workgroup gave up waiting.
+__device__ float grid_max_wave0(float wg_max, unsigned long long leaf_count, char* __restrict__ ws,
                                 unsigned spin_limit) {
   const int lane = threadIdx.x & 63;
-  const unsigned epoch = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(call)) + 1;
+  const unsigned long long v =
+      (static_cast<unsigned long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(leaf_count >> 32)))
+       << 32) | __builtin_amdgcn_readfirstlane(static_cast<unsigned>(leaf_count));
+  const unsigned epoch = static_cast<unsigned>((v - 1) / kLeafWgs) + 1;   // call number + 1
   if (lane == 0)
     store_agent(slot_of(ws, blockIdx.x), (static_cast<unsigned long long>(epoch) << 32) | __float_as_uint(wg_max));
+  if (blockIdx.x == 0)   // the slots beyond the grid take this call's epoch too
+    for (unsigned j = gridDim.x + lane; j < kMaxSlots; j += 64)
+      store_agent(slot_of(ws, j), static_cast<unsigned long long>(epoch) << 32);
   unsigned m = 0, spins = 0;
   while (true) {
     bool ok = true;
@@ -683,9 +698,9 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
     const int64_t t = wid + i * nw;
     load_tile_mfma<B, true>(x, t < ntiles ? t : ntiles - 1, nblocks, xr[i]);
   }
-  // the barrier's call number, counted while the loads are in flight
-  unsigned long long call = 0;
-  if (threadIdx.x < 64) call = count_arrival_wave0(ws);
+  // counted into the barrier while the loads are in flight
+  unsigned long long leaf = 0;
+  if (threadIdx.x < 64) leaf = arrive_wave0(ws);
   f32x4_t y[HOLD_Y ? TPW : 1][NM];
   float al[TPW];
   float amax = 0.0f;
@@ -708,7 +723,7 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
   }
   const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x < 64) {
-    const float A = grid_max_wave0(wg, call, ws, spin_limit);
+    const float A = grid_max_wave0(wg, leaf, ws, spin_limit);
     if (threadIdx.x == 0) amax_sh = A;
   }
   __syncthreads();
@@ -755,6 +770,38 @@ struct LdsTile {
   static __device__ __forceinline__ int swz(int n) { return B == 64 ? (n >> 1) & 7 : n & 15; }
 };
 
+// One gfx950 direct-to-LDS copy: lane i writes the 16 bytes at g to LDS
+// address lds + 16 i (lds is wave-uniform, in m0), non-temporal like the
+// direct loads.  Written as inline asm because with the compiler's builtin it
+// waits for every copy in flight before the wavefront's first LDS read
+// (vmcnt(0)), which serialises each tile's rotation behind all of the
+// wavefront's copies; the caller waits instead with wait_copies, tile by
+// tile.  One wait state separates the write of m0 from the copy that reads
+// it.  No VGPR is written, and the address VGPRs are read at issue.  Nothing
+// else in these kernels uses m0.
+__device__ __forceinline__ void copy16_to_lds(const uint4* g, unsigned lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+#endif
+}
+
+// Waits until at most N vector memory operations of the wavefront are in
+// flight.  Loads complete in issue order, so after the copies of tiles
+// 0..i and then of N / kCopies more tiles, wait_copies<N> means tiles 0..i
+// have landed (earlier operations, such as the barrier's leaf add and load,
+// only make it wait longer).  The memory clobber keeps the LDS reads after it;
+// the scheduling barrier keeps the previous tile's matrix and vector work
+// before it (the scheduler would otherwise sink some of it below the wait).
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
 // Copies tile t (clamped by the caller) into lds_tile; blocks past the end of
 // the tensor are filled with the tile's last block, as load_tile_mfma does.
 template <int B>
@@ -764,17 +811,14 @@ __device__ __forceinline__ void copy_tile_to_lds(const uint4* __restrict__ x, in
   const int lane = threadIdx.x & 63;
   const int rv = rows_valid(t, nblocks);
   const uint4* tile = x + t * (kTileBlocks * C16);
+  const unsigned base = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_tile)));
 #pragma unroll
   for (int d = 0; d < LdsTile<B>::kCopies; ++d) {
     const int pos = 64 * d + lane;
     const int n = pos / C16, p = pos % C16;
     const int row = n < rv ? n : rv - 1;
-    // cache policy 2: non-temporal, as the direct loads (the builtin exists
-    // in the device pass only)
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_global_load_lds(tile + row * C16 + (p ^ LdsTile<B>::swz(n)),
-                                     (__attribute__((address_space(3))) void*)(lds_tile + 1024 * d), 16, 0, 2);
-#endif
+    copy16_to_lds(tile + row * C16 + (p ^ LdsTile<B>::swz(n)), base + 1024 * d);
   }
 }
 
@@ -793,6 +837,7 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_lds_kernel(
     float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q, unsigned spin_limit) {
   constexpr int NK = B / 32, NM = B / 16, SROW = Blk<B>::kCodeRowMfma, TB = LdsTile<B>::kBytes;
   static_assert(WAVES * TPW * TB <= 128 * 1024, "x tiles exceed the LDS budget");
+  static_assert(TPW <= 4, "wait_copies is written out for up to 4 tiles");
   static_assert(kTileBlocks * SROW <= TB, "the code tile is staged in the first x tile");
   __shared__ float red[WAVES];
   __shared__ float amax_sh;
@@ -803,16 +848,17 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_lds_kernel(
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + (threadIdx.x >> 6);
   const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
+  // counted into the barrier first: its add returns nothing and its load is
+  // not waited for before the barrier
+  unsigned long long leaf = 0;
+  if (threadIdx.x < 64) leaf = arrive_wave0(ws);
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int64_t t = wid + i * nw;
     copy_tile_to_lds<B>(x, t < ntiles ? t : ntiles - 1, nblocks, xlds + i * TB);
   }
-  // the barrier's call number, counted while the copies are in flight
-  unsigned long long call = 0;
-  if (threadIdx.x < 64) call = count_arrival_wave0(ws);
-  // the copies of this wavefront have landed in LDS (vmcnt(0))
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // Tile i is rotated as soon as its own copies have landed, while the later
+  // tiles' copies are still in flight.
   f32x4_t y[TPW][NM];
   float al[TPW];
   float amax = 0.0f;
@@ -821,10 +867,13 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_lds_kernel(
     const int64_t t = wid + i * nw;
     const int64_t tc = t < ntiles ? t : ntiles - 1;
     const int rv = rows_valid(tc, nblocks);
+    if (i == 0) wait_copies<(TPW - 1) * LdsTile<B>::kCopies>();
+    if (i == 1) wait_copies<(TPW > 2 ? TPW - 2 : 0) * LdsTile<B>::kCopies>();
+    if (i == 2) wait_copies<(TPW > 3 ? TPW - 3 : 0) * LdsTile<B>::kCopies>();
+    if (i == 3) wait_copies<0>();
     uint4 xr[NK];
     read_tile_from_lds<B>(xlds + i * TB, xr);
     al[i] = ash_scale(column_sum_squares<B>(xr), sqrt_eb);
-    alpha[tc * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
     float m = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) {
@@ -835,9 +884,18 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_lds_kernel(
     }
     if (t < ntiles && n < rv) amax = fmaxf(amax, m * (al[i] * Blk<B>::rsqrt_b));
   }
+  // alpha after every tile's copies (a store in flight would count in the
+  // waits above)
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    const int64_t tc = t < ntiles ? t : ntiles - 1;
+    const int rv = rows_valid(tc, nblocks);
+    alpha[tc * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
+  }
   const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x < 64) {
-    const float A = grid_max_wave0(wg, call, ws, spin_limit);
+    const float A = grid_max_wave0(wg, leaf, ws, spin_limit);
     if (threadIdx.x == 0) amax_sh = A;
   }
   __syncthreads();
@@ -1192,10 +1250,10 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
   }
   const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x < 64) {
-    // counted here rather than at the start: a call number held across the
+    // counted here rather than at the start: a leaf count held across the
     // parts' accumulation made the allocator spill (B = 128, 2 tiles)
-    const unsigned long long call = count_arrival_wave0(ws);
-    const float A = grid_max_wave0(wg, call, ws, spin_limit);
+    const unsigned long long leaf = arrive_wave0(ws);
+    const float A = grid_max_wave0(wg, leaf, ws, spin_limit);
     if (threadIdx.x == 0) amax_sh = A;
   }
   __syncthreads();
@@ -1319,12 +1377,23 @@ __global__ __launch_bounds__(64 * WAVES) void compress_streaming_kernel(
 // near-zero values of TP tensors to the same integer] and a fallback for
 // consumers without FP8.  A = max|x| over the tensor or over a block of B
 // consecutive elements of a row, s = fp32(127 / A) (1 if A = 0),
-// code = clamp(rne(fp32(x s)), +-127), x_hat = bf16(fp32(code * fp32(1 / s))).
+// code = clamp(round_half_even(x s)), +-127) of the exact product, and
+// x_hat = bf16_RNE(code / s) of the exact quotient: both roundings are
+// decided exactly (int8_code, int8_to_bf16), not on an fp32 intermediate.
 // No ASH and no rotation.  Streaming kernels: each lane owns 8 consecutive
 // bf16 values (one 16-byte load) and their 8 codes (one 8-byte store); a
 // workgroup covers kInt8Unroll x 256 consecutive 16-byte pieces per trip.
 
 constexpr int kInt8Unroll = 4;
+
+// Keeps a trip's loads ahead of every use of them: without it the scheduler
+// may place the first use right after the first load, and the wait for it
+// then holds back the issue of the others.
+__device__ __forceinline__ void all_loads_issued() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
 
 // max |x| of 8 bf16 values as a bf16 bit pattern (non-negative bf16 values
 // order like their bits).
@@ -1340,26 +1409,121 @@ __device__ __forceinline__ float int8_scale_of(float amax) {
   return amax == 0.0f ? 1.0f : 127.0f / amax;
 }
 
+// clamp(round_half_even(x s), +-127) of the exact product.  p = fp32(x s) and
+// e = x s - p exactly (one fma: x has at most 8 significant bits and s 24, so
+// the product has at most 32 and the residual fits in fp32).  rint(p) can
+// differ from the exact rounding only where p lies exactly half-way between
+// two integers while x s does not (rounding to fp32 moves a value onto a
+// half-integer, never across one); there the sign of e decides.  Contraction
+// is off: fusing x * s into p - r would change the half-way test.
+__device__ __forceinline__ float int8_code(float x, float s) {
+#pragma clang fp contract(off)
+  const float p = x * s;
+  const float e = fmaf(x, s, -p);
+  const float r = __builtin_rintf(p);
+  const float d = p - r;
+  const float adj = (d == 0.5f && e > 0.0f) ? 1.0f : ((d == -0.5f && e < 0.0f) ? -1.0f : 0.0f);
+  return fminf(fmaxf(r + adj, -127.0f), 127.0f);
+}
+
+// The same code when the fp32 product is not exactly half-way between two
+// integers: then rint(fp32(x s)) is the exact rounding.
+__device__ __forceinline__ float int8_code_fast(float x, float s) {
+  return __builtin_amdgcn_fmed3f(__builtin_rintf(x * s), -127.0f, 127.0f);
+}
+
+// Whether any of the 8 bf16 values in v has an fp32 product with s that lies
+// exactly half-way between two integers (the only case int8_code_fast can get
+// wrong).
+__device__ __forceinline__ bool int8_half_way(const uint4 v, float s) {
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+  bool h = false;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h |= __builtin_amdgcn_fractf(__uint_as_float(w[i] << 16) * s) == 0.5f;
+    h |= __builtin_amdgcn_fractf(__uint_as_float(w[i] & 0xFFFF0000u) * s) == 0.5f;
+  }
+  return h;
+}
+
 // The two int8 codes of the bf16 pair in w, in the low 16 bits (element 0 first).
+template <bool EXACT>
 __device__ __forceinline__ unsigned int8_pair(unsigned w, float s) {
-  const float lo = fminf(fmaxf(__builtin_rintf(__uint_as_float(w << 16) * s), -127.0f), 127.0f);
-  const float hi = fminf(fmaxf(__builtin_rintf(__uint_as_float(w & 0xFFFF0000u) * s), -127.0f), 127.0f);
+  const float a = __uint_as_float(w << 16), b = __uint_as_float(w & 0xFFFF0000u);
+  const float lo = EXACT ? int8_code(a, s) : int8_code_fast(a, s);
+  const float hi = EXACT ? int8_code(b, s) : int8_code_fast(b, s);
   return (static_cast<unsigned>(static_cast<int>(lo)) & 0xFFu) |
          ((static_cast<unsigned>(static_cast<int>(hi)) & 0xFFu) << 8);
 }
 
+template <bool EXACT>
 __device__ __forceinline__ uint2 int8_codes_bf16x8(const uint4 v, float s) {
-  return make_uint2(int8_pair(v.x, s) | (int8_pair(v.y, s) << 16), int8_pair(v.z, s) | (int8_pair(v.w, s) << 16));
+  return make_uint2(int8_pair<EXACT>(v.x, s) | (int8_pair<EXACT>(v.y, s) << 16),
+                    int8_pair<EXACT>(v.z, s) | (int8_pair<EXACT>(v.w, s) << 16));
 }
 
-__device__ __forceinline__ uint4 bf16x8_from_int8x8(const uint2 c, float r) {
-  float v[8];
+// The 8 codes of a 16-byte piece: fp32 products decide them unless one of the
+// wavefront's products lies exactly half-way between two integers (rare),
+// and then the wavefront decides this piece on the exact products.
+__device__ __forceinline__ uint2 int8_codes_piece(const uint4 v, float s) {
+  if (__builtin_amdgcn_ballot_w64(int8_half_way(v, s)) != 0) return int8_codes_bf16x8<true>(v, s);
+  return int8_codes_bf16x8<false>(v, s);
+}
+
+// bf16_RNE(c / s) of the exact quotient, for an integer code c and s > 0
+// (r = fp32(1 / s)).  |c| r lies within 2^-23 (relative) of |c| / s, far
+// inside half a bf16 step, so the correctly rounded bf16 value is the
+// truncation t of |c| r or its successor.  The midpoint m between them is an
+// fp32 value, and |c| - m s, formed by one fma (exact product, one rounding),
+// has the sign of |c| / s - m: above m rounds up, exactly m rounds to the
+// even one of the two.
+__device__ __forceinline__ unsigned int8_to_bf16(int c, float s, float r) {
+  const float a = static_cast<float>(c < 0 ? -c : c);
+  const unsigned t = __float_as_uint(a * r) >> 16;
+  const float m = __uint_as_float((t << 16) | 0x8000u);
+  const float d = fmaf(-m, s, a);
+  const unsigned up = (d > 0.0f || (d == 0.0f && (t & 1u))) ? 1u : 0u;
+  return (t + up) | (c < 0 ? 0x8000u : 0u);
+}
+
+// The 8 codes of c as fp32 values.
+__device__ __forceinline__ void int8x8_values(const uint2 c, float (&v)[8]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     v[j] = static_cast<float>(static_cast<int8_t>((c.x >> (8 * j)) & 0xFFu));
     v[4 + j] = static_cast<float>(static_cast<int8_t>((c.y >> (8 * j)) & 0xFFu));
   }
-  return to_bf16x8(v, r);
+}
+
+// Whether any fp32 product code * r of the 8 codes lies within 3 fp32 steps
+// of a bf16 midpoint (low 16 bits within 0x8000 +- 3).  |code| r is within 2
+// steps of |code| / s, so elsewhere the bf16 rounding of the fp32 product is
+// the rounding of the exact quotient.
+__device__ __forceinline__ bool int8_near_midpoint(const float (&v)[8], float r) {
+  bool near = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) near |= ((__float_as_uint(v[j] * r) & 0xFFFFu) - 0x7FFDu) < 7u;
+  return near;
+}
+
+template <bool EXACT>
+__device__ __forceinline__ uint4 bf16x8_from_int8x8(const float (&v)[8], float s, float r) {
+  if constexpr (!EXACT) return to_bf16x8(v, r);
+  unsigned h[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) h[j] = int8_to_bf16(static_cast<int>(v[j]), s, r);
+  return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+}
+
+// The 8 bf16 outputs of a piece of codes: the bf16 rounding of the fp32
+// product code * r is the correctly rounded quotient unless a product of the
+// wavefront lies near a bf16 midpoint (rare), and then the wavefront decides
+// this piece exactly.
+__device__ __forceinline__ uint4 bf16_piece_from_int8(const uint2 c, float s, float r) {
+  float v[8];
+  int8x8_values(c, v);
+  if (__builtin_amdgcn_ballot_w64(int8_near_midpoint(v, r)) != 0) return bf16x8_from_int8x8<true>(v, s, r);
+  return bf16x8_from_int8x8<false>(v, s, r);
 }
 
 // Per-tensor INT8, pass 1: each workgroup's max |x| into partial[blockIdx.x].
@@ -1373,8 +1537,9 @@ __global__ __launch_bounds__(kThreads) void int8_absmax_kernel(const uint4* __re
 #pragma unroll
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
-      v[u] = i < n16 ? x[i] : make_uint4(0, 0, 0, 0);
+      v[u] = x[i < n16 ? i : n16 - 1];      // branch-free: past the end, a copy of the last piece
     }
+    all_loads_issued();
 #pragma unroll
     for (int u = 0; u < kInt8Unroll; ++u) m = max(m, bf16x8_absmax_bits(v[u]));
   }
@@ -1398,12 +1563,14 @@ __global__ __launch_bounds__(kThreads) void int8_quant_tensor_kernel(
 #pragma unroll
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
-      v[u] = i < n16 ? x[i] : make_uint4(0, 0, 0, 0);
+      v[u] = x[i < n16 ? i : n16 - 1];      // branch-free: past the end, a copy of the last piece
     }
+    all_loads_issued();
 #pragma unroll
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
-      if (i < n16) store8<TACO_NT_CODE_STORES != 0>(&q[i], int8_codes_bf16x8(v[u], s));
+      const uint2 c = int8_codes_piece(v[u], s);
+      if (i < n16) store8<TACO_NT_CODE_STORES != 0>(&q[i], c);
     }
   }
 }
@@ -1412,7 +1579,9 @@ __global__ __launch_bounds__(kThreads) void int8_quant_tensor_kernel(
 // every trip starts on a wavefront boundary, so no block straddles two
 // wavefronts); its max is an xor-shuffle over the group.  The trip loop is
 // uniform over the workgroup, and a group lies entirely inside or outside
-// the tensor, so the shuffles only read lanes of the same, valid group.
+// the tensor, so the shuffles of a group inside it only read lanes of the
+// same group (a group outside it reads copies of the last piece and stores
+// nothing).
 template <int G>
 __global__ __launch_bounds__(kThreads) void int8_quant_block_kernel(
     const uint4* __restrict__ x, int64_t n16, float* __restrict__ scale, uint2* __restrict__ q) {
@@ -1423,8 +1592,9 @@ __global__ __launch_bounds__(kThreads) void int8_quant_block_kernel(
 #pragma unroll
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
-      v[u] = i < n16 ? x[i] : make_uint4(0, 0, 0, 0);
+      v[u] = x[i < n16 ? i : n16 - 1];      // branch-free: past the end, a copy of the last piece
     }
+    all_loads_issued();
 #pragma unroll
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
@@ -1432,8 +1602,9 @@ __global__ __launch_bounds__(kThreads) void int8_quant_block_kernel(
 #pragma unroll
       for (int o = 1; o < G; o <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), o)));
       const float s = int8_scale_of(__uint_as_float(m << 16));
+      const uint2 c = int8_codes_piece(v[u], s);
       if (i < n16) {
-        store8<TACO_NT_CODE_STORES != 0>(&q[i], int8_codes_bf16x8(v[u], s));
+        store8<TACO_NT_CODE_STORES != 0>(&q[i], c);
         if (lane % G == 0) scale[i / G] = s;
       }
     }
@@ -1445,7 +1616,8 @@ __global__ __launch_bounds__(kThreads) void int8_quant_block_kernel(
 template <int G>
 __global__ __launch_bounds__(kThreads) void int8_dequant_kernel(
     const uint2* __restrict__ q, const float* __restrict__ scale, int64_t n16, uint4* __restrict__ out) {
-  const float r0 = G == 0 ? 1.0f / *scale : 1.0f;
+  const float s0 = G == 0 ? *scale : 1.0f;
+  const float r0 = 1.0f / s0;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads * kInt8Unroll;
   for (int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * kInt8Unroll; base < n16; base += stride) {
     uint2 c[kInt8Unroll];
@@ -1453,15 +1625,17 @@ __global__ __launch_bounds__(kThreads) void int8_dequant_kernel(
 #pragma unroll
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
-      c[u] = i < n16 ? q[i] : make_uint2(0, 0);
-      if constexpr (G != 0) sk[u] = i < n16 ? scale[i / G] : 1.0f;
+      const int64_t ic = i < n16 ? i : n16 - 1;   // branch-free loads, as above
+      c[u] = q[ic];
+      if constexpr (G != 0) sk[u] = scale[ic / G];
       else sk[u] = 1.0f;
     }
+    all_loads_issued();
 #pragma unroll
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
-      const float r = G == 0 ? r0 : 1.0f / sk[u];
-      if (i < n16) store16<TACO_NT_OUT_STORES != 0>(&out[i], bf16x8_from_int8x8(c[u], r));
+      const uint4 o = G == 0 ? bf16_piece_from_int8(c[u], s0, r0) : bf16_piece_from_int8(c[u], sk[u], 1.0f / sk[u]);
+      if (i < n16) store16<TACO_NT_OUT_STORES != 0>(&out[i], o);
     }
   }
 }
@@ -1516,8 +1690,6 @@ int resident_grid(Kernel kernel, int threads) {
 
 taco_status_t launched() { return hipGetLastError() == hipSuccess ? TACO_OK : TACO_ERR_HIP; }
 
-std::atomic<int> g_engine{TACO_ENGINE_AUTO};   // rotation engine of taco_compress (process-wide)
-std::atomic<unsigned> g_spin_limit{kDefaultSpinLimit};   // barrier poll bound (process-wide)
 
 // Launches the fused compress with TPW tiles per wavefront if every one of its
 // wavefronts can be resident at once (and the barrier has leaves for them).
@@ -1529,12 +1701,12 @@ std::atomic<unsigned> g_spin_limit{kDefaultSpinLimit};   // barrier poll bound (
 // tiles spread unevenly 9.4 us, cold).
 int fused_grid_cap(int resident) {
   const int cus = device_cu_count();
-  return std::min({resident, cus > 0 ? cus : resident, kLeaves * kLeafWgs});
+  return std::min({resident, cus > 0 ? cus : resident, kMaxSlots});
 }
 
 template <int B, int TPW, bool HOLD_Y, int WAVES>
 bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, char* ws,
-               uint4* q, hipStream_t stream, bool launch) {
+               uint4* q, hipStream_t stream, bool launch, unsigned polls) {
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
   if constexpr (HOLD_Y && B <= 128 && TACO_FUSED_LDS != 0) {   // these configurations stage x through LDS
@@ -1542,13 +1714,13 @@ bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, flo
     if (g > cap) return false;
     if (launch)
       hipLaunchKernelGGL((compress_fused_lds_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
-                         stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
+                         stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, polls);
   } else {
     static const int cap = fused_grid_cap(resident_grid(compress_fused_kernel<B, TPW, HOLD_Y, WAVES>, 64 * WAVES));
     if (g > cap) return false;
     if (launch)
       hipLaunchKernelGGL((compress_fused_kernel<B, TPW, HOLD_Y, WAVES>), dim3(g), dim3(64 * WAVES), 0,
-                         stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
+                         stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, polls);
   }
   return true;
 }
@@ -1563,35 +1735,33 @@ bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, flo
 // MFMA sequence per tile, so all give identical results.
 template <int B>
 bool launch_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, char* ws,
-                  uint4* q, hipStream_t stream, bool launch = true) {
-  if (try_fused<B, 1, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
+                  uint4* q, hipStream_t stream, bool launch, unsigned polls) {
+  if (try_fused<B, 1, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
   if constexpr (B <= 128)
-    if (try_fused<B, 2, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
+    if (try_fused<B, 2, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
   if constexpr (B == 64) {
-    if (try_fused<B, 4, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
-    if (try_fused<B, 6, false, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
+    if (try_fused<B, 4, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
+    if (try_fused<B, 6, false, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
   }
   if constexpr (B == 128) {
-    if (try_fused<B, 3, false, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
-    if (try_fused<B, 4, false, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
+    if (try_fused<B, 3, false, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
+    if (try_fused<B, 4, false, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
   }
   if constexpr (B == 256)   // 8 wavefronts per CU: 226 VGPRs
-    if (try_fused<B, 4, false, kWavesC / 2>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch)) return true;
+    if (try_fused<B, 4, false, kWavesC / 2>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
   return false;
 }
 
-std::atomic<bool> g_single_pass{true};   // fused compress when the tensor fits (process-wide)
-
 template <int B>
 void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, float* alpha,
-                     float* scale, void* workspace, hipStream_t stream) {
+                     float* scale, void* workspace, hipStream_t stream, bool single_pass, unsigned polls) {
   const float sqrt_eb = static_cast<float>(sqrt(static_cast<double>(energy) * B));
   const uint4* xv = static_cast<const uint4*>(x);
   uint4* qv = reinterpret_cast<uint4*>(q);
   char* ws = static_cast<char*>(workspace);
   float* partial = reinterpret_cast<float*>(ws + kPartialOffset);
   // Single fused pass when the tensor fits in the resident wavefronts' VGPRs.
-  if (g_single_pass.load() && launch_fused<B>(xv, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
+  if (single_pass && launch_fused<B>(xv, nblocks, sqrt_eb, alpha, scale, ws, qv, stream, true, polls)) return;
   constexpr int U = 2;
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t per_wg = static_cast<int64_t>(kWaves) * U;
@@ -1636,18 +1806,19 @@ void launch_decompress_sum(const Parts& parts, int nparts, int64_t nblocks, void
 // Bytes of the compress workspace proper (barrier lines and partial maxima),
 // rounded up so that the decompress-sum-compress intermediate after it is
 // 256-byte aligned.
-constexpr size_t kCompressWorkspace = (kSlotOffset + kSlotStride * kLeaves * kLeafWgs + 255) / 256 * 256;
+constexpr size_t kCompressWorkspace = (kSlotOffset + static_cast<size_t>(kSlotStride) * kMaxSlots + 255) / 256 * 256;
 
 template <int B, int TPW, int WAVES>
 bool try_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblocks, float sqrt_eb,
-                                 float* alpha, float* scale, char* ws, uint4* q, hipStream_t stream) {
+                                 float* alpha, float* scale, char* ws, uint4* q, hipStream_t stream,
+                                 unsigned polls) {
   static const int cap = std::min(resident_grid(decompress_sum_compress_kernel<B, TPW, WAVES>, 64 * WAVES),
-                                  kLeaves * kLeafWgs);
+                                  kMaxSlots);
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
   if (g > cap) return false;
   hipLaunchKernelGGL((decompress_sum_compress_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
-                     stream, parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, q, g_spin_limit.load());
+                     stream, parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, q, polls);
   return true;
 }
 
@@ -1657,26 +1828,26 @@ bool try_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblocks
 template <int B>
 void launch_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblocks, float energy,
                                     uint8_t* q, float* alpha, float* scale, void* workspace,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, bool single_pass, unsigned polls) {
   const float sqrt_eb = static_cast<float>(sqrt(static_cast<double>(energy) * B));
   char* ws = static_cast<char*>(workspace);
   uint4* qv = reinterpret_cast<uint4*>(q);
   // 16 wavefronts per CU (128 VGPRs each) up to B = 128; at B = 256 the
   // rotation of the sum needs more registers, so 8 wavefronts (256 VGPRs),
   // two tiles each.
-  if (g_single_pass.load()) {
+  if (single_pass) {
     if constexpr (B <= 128) {
-      if (try_decompress_sum_compress<B, 1, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
-      if (try_decompress_sum_compress<B, 2, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
+      if (try_decompress_sum_compress<B, 1, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream, polls)) return;
+      if (try_decompress_sum_compress<B, 2, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream, polls)) return;
     } else {
-      if (try_decompress_sum_compress<B, 2, kWavesC / 2>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
+      if (try_decompress_sum_compress<B, 2, kWavesC / 2>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream, polls)) return;
     }
     if constexpr (B == 64)
-      if (try_decompress_sum_compress<B, 4, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream)) return;
+      if (try_decompress_sum_compress<B, 4, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream, polls)) return;
   }
   void* sum = ws + kCompressWorkspace;
   launch_decompress_sum<B>(parts, nparts, nblocks, sum, stream);
-  launch_compress<B>(sum, nblocks, energy, q, alpha, scale, workspace, stream);
+  launch_compress<B>(sum, nblocks, energy, q, alpha, scale, workspace, stream, single_pass, polls);
 }
 
 template <int B, int MODE>
@@ -1739,6 +1910,43 @@ void launch_decompress_int8(const int8_t* q, const float* scale, int64_t n16, in
   }
 }
 
+// A byte range of a caller's buffer, for the aliasing checks.
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+bool overlap(const Span& a, const Span& b) {
+  if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Whether an output overlaps another output or an input (inputs may overlap
+// each other: they are only read).
+bool aliased(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (auto i = outs.begin(); i != outs.end(); ++i) {
+    for (auto j = i + 1; j != outs.end(); ++j)
+      if (overlap(*i, *j)) return true;
+    for (const Span& in : ins)
+      if (overlap(*i, in)) return true;
+  }
+  return false;
+}
+
+bool parts_overlap(const Span& out, const Parts& parts, int nparts, size_t qn, size_t an) {
+  for (int p = 0; p < nparts; ++p)
+    if (overlap(out, {parts.q[p], qn}) || overlap(out, {parts.alpha[p], an}) || overlap(out, {parts.scale[p], 4}))
+      return true;
+  return false;
+}
+
+bool energy_ok(float e) { return e >= kMinEnergy && e <= kMaxEnergy; }
+
+taco_status_t check_flags(uint32_t flags) {
+  return (flags & ~static_cast<uint32_t>(TACO_FLAG_TWO_PASS)) == 0 ? TACO_OK : TACO_ERR_FLAGS;
+}
+
 }  // namespace
 
 // ----------------------------------------------------------------- C ABI
@@ -1756,54 +1964,31 @@ const char* taco_status_string(taco_status_t status) {
     case TACO_ERR_WORKSPACE: return "TACO_ERR_WORKSPACE: workspace too small";
     case TACO_ERR_BAD_NPARTS: return "TACO_ERR_BAD_NPARTS: nparts must be in [1, 8]";
     case TACO_ERR_HIP: return "TACO_ERR_HIP: a HIP call or kernel launch failed";
-    case TACO_ERR_BAD_ENGINE: return "TACO_ERR_BAD_ENGINE: unknown rotation engine";
-    case TACO_ERR_ALIAS: return "TACO_ERR_ALIAS: an output buffer is also an input";
+    case TACO_ERR_FLAGS: return "TACO_ERR_FLAGS: unknown bit in flags";
+    case TACO_ERR_ALIAS: return "TACO_ERR_ALIAS: an output buffer overlaps an input or another output";
   }
   return "TACO_ERR_UNKNOWN";
 }
 
-const char* taco_version(void) { return "0.3.0"; }
-
-taco_status_t taco_set_rotation_engine(taco_engine_t engine) {
-  // The VALU compress engine has been removed: its kernels took a GPU memory
-  // fault on a 3-tile tensor whose cause was not found.  Only the MFMA engine
-  // remains.
-  if (engine == TACO_ENGINE_VALU) return TACO_ERR_BAD_ENGINE;
-  if (engine != TACO_ENGINE_AUTO && engine != TACO_ENGINE_MFMA) return TACO_ERR_BAD_ENGINE;
-  g_engine.store(engine);
-  return TACO_OK;
-}
-
-taco_engine_t taco_get_rotation_engine(void) { return static_cast<taco_engine_t>(g_engine.load()); }
-
-void taco_set_single_pass(int enable) { g_single_pass.store(enable != 0); }
-
-int taco_get_single_pass(void) { return g_single_pass.load() ? 1 : 0; }
+const char* taco_version(void) { return "0.4.0"; }
 
 int taco_compress_is_single_pass(int64_t tokens, int64_t hidden, int32_t block) {
   if (check_shape(tokens, hidden, block) != TACO_OK || device_cu_count() <= 0) return -1;
-  if (!g_single_pass.load()) return 0;
   const int64_t nblocks = tokens * (hidden / block);
   bool fits;
   switch (block) {
-    case 64: fits = launch_fused<64>(nullptr, nblocks, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, false); break;
-    case 128: fits = launch_fused<128>(nullptr, nblocks, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, false); break;
-    default: fits = launch_fused<256>(nullptr, nblocks, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, false); break;
+    case 64: fits = launch_fused<64>(nullptr, nblocks, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, false, 0); break;
+    case 128: fits = launch_fused<128>(nullptr, nblocks, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, false, 0); break;
+    default: fits = launch_fused<256>(nullptr, nblocks, 0.0f, nullptr, nullptr, nullptr, nullptr, nullptr, false, 0); break;
   }
   return fits ? 1 : 0;
 }
 
-void taco_set_barrier_spin_limit(uint32_t polls) {
-  g_spin_limit.store(polls == 0 ? kDefaultSpinLimit : polls);
-}
-
-uint32_t taco_get_barrier_spin_limit(void) { return g_spin_limit.load(); }
-
-taco_status_t taco_workspace_timed_out(const void* workspace, void* stream, int* timed_out) {
+taco_status_t taco_workspace_timed_out(const void* workspace, taco_stream_t stream, int* timed_out) {
   if (workspace == nullptr || timed_out == nullptr) return TACO_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TACO_ERR_ALIGN;
   unsigned flag = 0;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const char* root = static_cast<const char*>(workspace) + offsetof(RootLine, timed_out);
   if (hipMemcpyAsync(&flag, root, sizeof(flag), hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess)
@@ -1822,26 +2007,41 @@ size_t taco_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t blo
   return kCompressWorkspace;   // leaf lines, partial maxima and barrier slots
 }
 
-taco_status_t taco_compress(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,
-                            float target_energy, uint8_t* q_fp8, float* alpha, float* scale,
-                            void* workspace, size_t workspace_bytes, taco_stream_t stream) {
+taco_status_t taco_compress_ex(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,
+                               float target_energy, uint8_t* q_fp8, float* alpha, float* scale,
+                               void* workspace, size_t workspace_bytes, uint32_t flags,
+                               uint32_t barrier_polls, taco_stream_t stream) {
   if (!x_bf16 || !q_fp8 || !alpha || !scale || !workspace) return TACO_ERR_NULL;
   const taco_status_t st = check_shape(tokens, hidden, block);
   if (st != TACO_OK) return st;
   if (!aligned(x_bf16, 16) || !aligned(q_fp8, 16) || !aligned(alpha, 4) || !aligned(scale, 4) ||
       !aligned(workspace, 256))
     return TACO_ERR_ALIGN;
-  if (!(target_energy >= kMinEnergy && target_energy <= kMaxEnergy)) return TACO_ERR_BAD_ENERGY;
+  if (!energy_ok(target_energy)) return TACO_ERR_BAD_ENERGY;
   if (workspace_bytes < taco_compress_workspace_bytes(tokens, hidden, block)) return TACO_ERR_WORKSPACE;
-  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  if (check_flags(flags) != TACO_OK) return TACO_ERR_FLAGS;
   const int64_t nblocks = tokens * (hidden / block);
+  const size_t n = static_cast<size_t>(tokens) * static_cast<size_t>(hidden);
+  if (aliased({{q_fp8, n}, {alpha, 4 * static_cast<size_t>(nblocks)}, {scale, 4}, {workspace, workspace_bytes}},
+              {{x_bf16, 2 * n}}))
+    return TACO_ERR_ALIAS;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool single = (flags & TACO_FLAG_TWO_PASS) == 0;
+  const unsigned polls = barrier_polls == 0 ? kDefaultSpinLimit : barrier_polls;
   switch (block) {
-    case 64: launch_compress<64>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, workspace, s); break;
-    case 128: launch_compress<128>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, workspace, s); break;
-    default: launch_compress<256>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, workspace, s); break;
+    case 64: launch_compress<64>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, workspace, s, single, polls); break;
+    case 128: launch_compress<128>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, workspace, s, single, polls); break;
+    default: launch_compress<256>(x_bf16, nblocks, target_energy, q_fp8, alpha, scale, workspace, s, single, polls); break;
   }
   return launched();
+}
+
+taco_status_t taco_compress(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,
+                            float target_energy, uint8_t* q_fp8, float* alpha, float* scale,
+                            void* workspace, size_t workspace_bytes, taco_stream_t stream) {
+  return taco_compress_ex(x_bf16, tokens, hidden, block, target_energy, q_fp8, alpha, scale, workspace,
+                          workspace_bytes, 0, 0, stream);
 }
 
 taco_status_t taco_decompress(const uint8_t* q_fp8, const float* alpha, const float* scale,
@@ -1852,8 +2052,11 @@ taco_status_t taco_decompress(const uint8_t* q_fp8, const float* alpha, const fl
   if (st != TACO_OK) return st;
   if (!aligned(q_fp8, 16) || !aligned(y_bf16, 16) || !aligned(alpha, 4) || !aligned(scale, 4))
     return TACO_ERR_ALIGN;
-  if (device_cu_count() <= 0) return TACO_ERR_HIP;
   const int64_t nblocks = tokens * (hidden / block);
+  const size_t n = static_cast<size_t>(tokens) * static_cast<size_t>(hidden);
+  if (aliased({{y_bf16, 2 * n}}, {{q_fp8, n}, {alpha, 4 * static_cast<size_t>(nblocks)}, {scale, 4}}))
+    return TACO_ERR_ALIAS;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (block) {
     case 64: launch_decompress<64, false>(q_fp8, alpha, scale, nblocks, y_bf16, s); break;
@@ -1880,8 +2083,10 @@ taco_status_t taco_decompress_sum(const uint8_t* const* q_fp8, const float* cons
     parts.scale[p] = scale[p];
   }
   if (!aligned(out_bf16, 16)) return TACO_ERR_ALIGN;
-  if (device_cu_count() <= 0) return TACO_ERR_HIP;
   const int64_t nblocks = tokens * (hidden / block);
+  const size_t n = static_cast<size_t>(tokens) * static_cast<size_t>(hidden);
+  if (parts_overlap({out_bf16, 2 * n}, parts, nparts, n, 4 * static_cast<size_t>(nblocks))) return TACO_ERR_ALIAS;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (block) {
     case 64: launch_decompress_sum<64>(parts, nparts, nblocks, out_bf16, s); break;
@@ -1906,6 +2111,10 @@ taco_status_t taco_compress_int8(const void* x_bf16, int64_t tokens, int64_t hid
       (block == 0 && !aligned(workspace, 256)))
     return TACO_ERR_ALIGN;
   if (block == 0 && workspace_bytes < kCompressWorkspace) return TACO_ERR_WORKSPACE;
+  const size_t n = static_cast<size_t>(tokens) * static_cast<size_t>(hidden);
+  const size_t sbytes = block == 0 ? 4 : 4 * (n / static_cast<size_t>(block));
+  if (aliased({{q_int8, n}, {scale, sbytes}, {block == 0 ? workspace : nullptr, workspace_bytes}}, {{x_bf16, 2 * n}}))
+    return TACO_ERR_ALIAS;
   if (device_cu_count() <= 0) return TACO_ERR_HIP;
   launch_compress_int8(x_bf16, tokens * hidden / 8, block, q_int8, scale, workspace,
                        reinterpret_cast<hipStream_t>(stream));
@@ -1918,6 +2127,9 @@ taco_status_t taco_decompress_int8(const int8_t* q_int8, const float* scale, int
   const taco_status_t st = check_shape_int8(tokens, hidden, block);
   if (st != TACO_OK) return st;
   if (!aligned(q_int8, 16) || !aligned(y_bf16, 16) || !aligned(scale, 4)) return TACO_ERR_ALIGN;
+  const size_t n = static_cast<size_t>(tokens) * static_cast<size_t>(hidden);
+  const size_t sbytes = block == 0 ? 4 : 4 * (n / static_cast<size_t>(block));
+  if (aliased({{y_bf16, 2 * n}}, {{q_int8, n}, {scale, sbytes}})) return TACO_ERR_ALIAS;
   if (device_cu_count() <= 0) return TACO_ERR_HIP;
   launch_decompress_int8(q_int8, scale, tokens * hidden / 8, block, y_bf16, reinterpret_cast<hipStream_t>(stream));
   return launched();
@@ -1928,22 +2140,21 @@ size_t taco_decompress_sum_compress_workspace_bytes(int64_t tokens, int64_t hidd
   return kCompressWorkspace + static_cast<size_t>(tokens) * static_cast<size_t>(hidden) * 2;
 }
 
-taco_status_t taco_decompress_sum_compress(const uint8_t* const* q_fp8, const float* const* alpha,
-                                           const float* const* scale, int32_t nparts, int64_t tokens,
-                                           int64_t hidden, int32_t block, float target_energy,
-                                           uint8_t* q_out, float* alpha_out, float* scale_out,
-                                           void* workspace, size_t workspace_bytes,
-                                           taco_stream_t stream) {
+taco_status_t taco_decompress_sum_compress_ex(const uint8_t* const* q_fp8, const float* const* alpha,
+                                              const float* const* scale, int32_t nparts, int64_t tokens,
+                                              int64_t hidden, int32_t block, float target_energy,
+                                              uint8_t* q_out, float* alpha_out, float* scale_out,
+                                              void* workspace, size_t workspace_bytes, uint32_t flags,
+                                              uint32_t barrier_polls, taco_stream_t stream) {
   if (!q_fp8 || !alpha || !scale || !q_out || !alpha_out || !scale_out || !workspace) return TACO_ERR_NULL;
   if (nparts < 1 || nparts > TACO_MAX_PARTS) return TACO_ERR_BAD_NPARTS;
   const taco_status_t st = check_shape(tokens, hidden, block);
   if (st != TACO_OK) return st;
-  if (!(target_energy >= kMinEnergy && target_energy <= kMaxEnergy)) return TACO_ERR_BAD_ENERGY;
+  if (!energy_ok(target_energy)) return TACO_ERR_BAD_ENERGY;
   Parts parts{};
   for (int p = 0; p < nparts; ++p) {
     if (!q_fp8[p] || !alpha[p] || !scale[p]) return TACO_ERR_NULL;
     if (!aligned(q_fp8[p], 16) || !aligned(alpha[p], 4) || !aligned(scale[p], 4)) return TACO_ERR_ALIGN;
-    if (q_fp8[p] == q_out || alpha[p] == alpha_out || scale[p] == scale_out) return TACO_ERR_ALIAS;
     parts.q[p] = reinterpret_cast<const uint4*>(q_fp8[p]);
     parts.alpha[p] = alpha[p];
     parts.scale[p] = scale[p];
@@ -1952,15 +2163,36 @@ taco_status_t taco_decompress_sum_compress(const uint8_t* const* q_fp8, const fl
     return TACO_ERR_ALIGN;
   if (workspace_bytes < taco_decompress_sum_compress_workspace_bytes(tokens, hidden, block))
     return TACO_ERR_WORKSPACE;
-  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  if (check_flags(flags) != TACO_OK) return TACO_ERR_FLAGS;
   const int64_t nblocks = tokens * (hidden / block);
+  const size_t n = static_cast<size_t>(tokens) * static_cast<size_t>(hidden);
+  const size_t an = 4 * static_cast<size_t>(nblocks);
+  const Span outs[4] = {{q_out, n}, {alpha_out, an}, {scale_out, 4}, {workspace, workspace_bytes}};
+  if (aliased({outs[0], outs[1], outs[2], outs[3]}, {}))
+    return TACO_ERR_ALIAS;
+  for (const Span& o : outs)
+    if (parts_overlap(o, parts, nparts, n, an)) return TACO_ERR_ALIAS;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool single = (flags & TACO_FLAG_TWO_PASS) == 0;
+  const unsigned polls = barrier_polls == 0 ? kDefaultSpinLimit : barrier_polls;
   switch (block) {
-    case 64: launch_decompress_sum_compress<64>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s); break;
-    case 128: launch_decompress_sum_compress<128>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s); break;
-    default: launch_decompress_sum_compress<256>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s); break;
+    case 64: launch_decompress_sum_compress<64>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s, single, polls); break;
+    case 128: launch_decompress_sum_compress<128>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s, single, polls); break;
+    default: launch_decompress_sum_compress<256>(parts, nparts, nblocks, target_energy, q_out, alpha_out, scale_out, workspace, s, single, polls); break;
   }
   return launched();
+}
+
+taco_status_t taco_decompress_sum_compress(const uint8_t* const* q_fp8, const float* const* alpha,
+                                           const float* const* scale, int32_t nparts, int64_t tokens,
+                                           int64_t hidden, int32_t block, float target_energy,
+                                           uint8_t* q_out, float* alpha_out, float* scale_out,
+                                           void* workspace, size_t workspace_bytes,
+                                           taco_stream_t stream) {
+  return taco_decompress_sum_compress_ex(q_fp8, alpha, scale, nparts, tokens, hidden, block, target_energy,
+                                         q_out, alpha_out, scale_out, workspace, workspace_bytes, 0, 0,
+                                         stream);
 }
 
 taco_status_t taco_compress_blockscale(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,
@@ -1971,9 +2203,12 @@ taco_status_t taco_compress_blockscale(const void* x_bf16, int64_t tokens, int64
     return TACO_ERR_ALIGN;
   const taco_status_t st = check_shape(tokens, hidden, block);
   if (st != TACO_OK) return st;
-  if (!(target_energy >= kMinEnergy && target_energy <= kMaxEnergy)) return TACO_ERR_BAD_ENERGY;
-  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  if (!energy_ok(target_energy)) return TACO_ERR_BAD_ENERGY;
   const int64_t nblocks = tokens * (hidden / block);
+  const size_t n = static_cast<size_t>(tokens) * static_cast<size_t>(hidden);
+  const size_t an = 4 * static_cast<size_t>(nblocks);
+  if (aliased({{q_fp8, n}, {alpha, an}, {scale_blk, an}}, {{x_bf16, 2 * n}})) return TACO_ERR_ALIAS;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (block) {
     case 64: launch_compress_streaming<64, kDsBlockGuard>(x_bf16, nblocks, target_energy, nullptr, q_fp8, alpha, scale_blk, nullptr, s); break;
@@ -1991,8 +2226,11 @@ taco_status_t taco_decompress_blockscale(const uint8_t* q_fp8, const float* alph
   if (st != TACO_OK) return st;
   if (!aligned(q_fp8, 16) || !aligned(y_bf16, 16) || !aligned(alpha, 4) || !aligned(scale_blk, 4))
     return TACO_ERR_ALIGN;
-  if (device_cu_count() <= 0) return TACO_ERR_HIP;
   const int64_t nblocks = tokens * (hidden / block);
+  const size_t n = static_cast<size_t>(tokens) * static_cast<size_t>(hidden);
+  const size_t an = 4 * static_cast<size_t>(nblocks);
+  if (aliased({{y_bf16, 2 * n}}, {{q_fp8, n}, {alpha, an}, {scale_blk, an}})) return TACO_ERR_ALIAS;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (block) {
     case 64: launch_decompress<64, true>(q_fp8, alpha, scale_blk, nblocks, y_bf16, s); break;
@@ -2009,12 +2247,16 @@ taco_status_t taco_compress_delayed(const void* x_bf16, int64_t tokens, int64_t 
   if (!aligned(x_bf16, 16) || !aligned(q_fp8, 16) || !aligned(alpha, 4) || !aligned(scale, 4) ||
       !aligned(amax_prev, 4) || !aligned(amax_out, 4))
     return TACO_ERR_ALIGN;
-  if (amax_prev == amax_out) return TACO_ERR_ALIAS;
   const taco_status_t st = check_shape(tokens, hidden, block);
   if (st != TACO_OK) return st;
-  if (!(target_energy >= kMinEnergy && target_energy <= kMaxEnergy)) return TACO_ERR_BAD_ENERGY;
-  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  if (!energy_ok(target_energy)) return TACO_ERR_BAD_ENERGY;
   const int64_t nblocks = tokens * (hidden / block);
+  const size_t n = static_cast<size_t>(tokens) * static_cast<size_t>(hidden);
+  constexpr size_t kAmaxBytes = 4 * TACO_AMAX_FLOATS;
+  if (aliased({{q_fp8, n}, {alpha, 4 * static_cast<size_t>(nblocks)}, {scale, 4}, {amax_out, kAmaxBytes}},
+              {{x_bf16, 2 * n}, {amax_prev, kAmaxBytes}}))
+    return TACO_ERR_ALIAS;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   switch (block) {
     case 64: launch_compress_streaming<64, kDsDelayed>(x_bf16, nblocks, target_energy, amax_prev, q_fp8, alpha, scale, amax_out, s); break;

@@ -31,6 +31,10 @@
  * stream) and returns; outputs are valid once the stream reaches that point.
  * Calls that share a workspace must not run concurrently on different streams.
  *
+ * Aliasing.  No output may overlap an input or another output (byte ranges
+ * of the sizes below); inputs may overlap each other.  A violation returns
+ * TACO_ERR_ALIAS.
+ *
  * Errors.  Arguments are checked before anything is enqueued; a failed check
  * returns a nonzero status and enqueues nothing.  TACO_ERR_HIP reports a
  * failed kernel launch (hipGetLastError).  A device fault surfaces at the
@@ -62,20 +66,14 @@ typedef enum {
   TACO_ERR_WORKSPACE = 6,         /* workspace smaller than required               */
   TACO_ERR_BAD_NPARTS = 7,        /* nparts outside [1, TACO_MAX_PARTS]            */
   TACO_ERR_HIP = 8,               /* a HIP runtime call or kernel launch failed    */
-  TACO_ERR_BAD_ENGINE = 9,        /* unknown value passed to taco_set_rotation_engine */
-  TACO_ERR_ALIAS = 10             /* an output buffer is also one of the inputs      */
+  TACO_ERR_FLAGS = 9,             /* an unknown bit in a flags argument            */
+  TACO_ERR_ALIAS = 10             /* an output overlaps an input or another output */
 } taco_status_t;
 
-/* How taco_compress evaluates the Hadamard rotation.  Both give the same
- * values up to fp32 rounding order (and so the same codes except at rounding
- * ties); they differ in which hardware unit does the work. */
-typedef enum {
-  TACO_ENGINE_AUTO = 0,           /* the faster one on this device (MFMA)          */
-  TACO_ENGINE_VALU = 1,           /* radix-2 butterflies on the vector ALUs + DPP;
-                                     currently disabled: selecting it returns
-                                     TACO_ERR_BAD_ENGINE                          */
-  TACO_ENGINE_MFMA = 2            /* +-1 contraction on the bf16 matrix cores      */
-} taco_engine_t;
+/* Flags of taco_compress_ex and taco_decompress_sum_compress_ex. */
+#define TACO_FLAG_TWO_PASS 1u
+/* Default bound on the grid barrier's polls (barrier_polls == 0). */
+#define TACO_DEFAULT_BARRIER_POLLS (1u << 16)
 
 #define TACO_MAX_PARTS 8
 /* amax buffers of taco_compress_delayed: TACO_AMAX_FLOATS fp32 (16 KiB) holding
@@ -89,26 +87,13 @@ typedef enum {
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* taco_status_string(taco_status_t status);
 
-/* Library version string, e.g. "0.3.0" (0.3: the barrier workspace grew to 37120 bytes). */
+/* Library version string, e.g. "0.4.0" (0.4: per-call pass structure and
+ * barrier bound; no process-wide settings). */
 const char* taco_version(void);
 
-/* Select the rotation engine of taco_compress for the whole process (it is
- * read when a call is made; calls already enqueued are unaffected).  Returns
- * TACO_ERR_BAD_ENGINE for an unknown value.  Default: TACO_ENGINE_AUTO. */
-taco_status_t taco_set_rotation_engine(taco_engine_t engine);
-taco_engine_t taco_get_rotation_engine(void);
-
-/* Pass structure of taco_compress for the whole process.  enable != 0 (the
- * default): one fused kernel that keeps the tensor in registers across a
- * grid-wide max whenever every tile fits in the resident wavefronts, two
- * kernels otherwise (statistics, then quantisation re-reading x).  enable == 0:
- * always the two kernels.  Both give identical results. */
-void taco_set_single_pass(int enable);
-int taco_get_single_pass(void);
-
-/* Whether taco_compress of this shape would run as the single fused kernel on
- * the current device with the current setting: 1 yes, 0 two kernels, -1 for
- * an invalid shape or no usable device.  The fused kernel holds the rotated
+/* Whether taco_compress of this shape runs as the single fused kernel on the
+ * current device: 1 yes, 0 two kernels, -1 for an invalid shape or no usable
+ * device.  The fused kernel holds the rotated
  * blocks in registers up to 16.8M elements, the bf16 input beyond that, up to
  * 25.2M elements at block 64 and 33.6M at blocks 128 and 256 on a 256-CU
  * MI355X; larger tensors take the two kernels. */
@@ -124,32 +109,32 @@ int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block);
  * workgroup) and per-workgroup partial maxima.
  * It must be zero-filled once when allocated; every call leaves it ready for
  * the next one.  Calls that share a workspace must be ordered (the same
- * stream).  While a single-pass compress runs no other kernel may occupy the
- * GPU's compute units: its workgroups must all be resident at once to pass the
- * barrier; a workgroup that is not gives up after a bounded wait (see
- * taco_set_barrier_spin_limit), and the codes of every workgroup that gave up
- * are E4M3 NaN (0x7F / 0xFF), so the failure cannot pass for a result
- * (taco_set_single_pass(0) removes the requirement).  A timeout also sets a
- * sticky flag in the workspace (taco_workspace_timed_out); the workspace stays
- * valid for later calls. */
+ * stream).
+ *
+ * Residency.  The single-pass kernel (taco_compress, and taco_compress_ex
+ * without TACO_FLAG_TWO_PASS) meets all its workgroups at a grid-wide barrier,
+ * so they must all be resident at once: its grid is at most one workgroup per
+ * compute unit, and no other kernel may hold compute units while it runs.  A
+ * caller that overlaps compression with other kernels (e.g. a collective on
+ * another stream) must pass TACO_FLAG_TWO_PASS, which never waits on another
+ * workgroup.  If residency fails anyway, a workgroup gives up after
+ * barrier_polls polls (TACO_DEFAULT_BARRIER_POLLS, tens of milliseconds, when
+ * 0 is passed; a resident grid passes the barrier in microseconds), writes its
+ * codes as E4M3 NaN (0x7F / 0xFF), so the failure cannot pass for a result,
+ * and sets a sticky flag in the workspace (taco_workspace_timed_out).  The
+ * fallback for the host: when the flag is set, clear it (zero the workspace)
+ * and compress the same input again with TACO_FLAG_TWO_PASS; the two paths
+ * give bitwise-identical results.  The workspace stays valid after a timeout. */
 size_t taco_compress_workspace_bytes(int64_t tokens, int64_t hidden, int32_t block);
-
-/* Bound on the polls of the single-pass kernels' grid barrier, for the whole
- * process (read when a call is made).  polls == 0 restores the default, 2^22
- * polls (seconds; a barrier whose workgroups are all resident completes in
- * microseconds).  A small bound makes waits give up early, e.g. to exercise
- * the timeout path in tests: every kernel still finishes. */
-void taco_set_barrier_spin_limit(uint32_t polls);
-uint32_t taco_get_barrier_spin_limit(void);
 
 /* Whether a single-pass call on this workspace (of taco_compress or
  * taco_decompress_sum_compress) has given up waiting at its grid barrier since
  * the workspace was zero-filled: *timed_out = 1 if so, else 0.  Waits for the
- * work queued on `stream` (a hipStream_t; NULL: the null stream) to finish, then
- * reads 4 bytes of the workspace.  The flag is sticky: zero-fill the workspace
- * to clear it.  TACO_ERR_NULL for a NULL pointer, TACO_ERR_ALIGN for a
- * workspace not 256-byte aligned, TACO_ERR_HIP if the copy fails. */
-taco_status_t taco_workspace_timed_out(const void* workspace, void* stream, int* timed_out);
+ * work queued on `stream` (NULL: the null stream) to finish, then reads 4
+ * bytes of the workspace.  The flag is sticky: zero-fill the workspace to
+ * clear it.  TACO_ERR_NULL for a NULL pointer, TACO_ERR_ALIGN for a workspace
+ * not 256-byte aligned, TACO_ERR_HIP if the copy fails. */
+taco_status_t taco_workspace_timed_out(const void* workspace, taco_stream_t stream, int* timed_out);
 
 /*
  * Compress: energy -> ASH scale -> Hadamard rotation -> DS scale -> FP8
@@ -161,11 +146,30 @@ taco_status_t taco_workspace_timed_out(const void* workspace, void* stream, int*
  *   alpha           out: fp32 [tokens, hidden / block]
  *   scale           out: fp32 [1]
  *   workspace       scratch of at least taco_compress_workspace_bytes() bytes
+ * One fused kernel when the tensor fits in the resident wavefronts (see
+ * Residency above and taco_compress_is_single_pass), two kernels otherwise.
+ * Same as taco_compress_ex with flags 0 and barrier_polls 0.
  */
 taco_status_t taco_compress(const void* x_bf16, int64_t tokens, int64_t hidden,
                             int32_t block, float target_energy, uint8_t* q_fp8,
                             float* alpha, float* scale, void* workspace,
                             size_t workspace_bytes, taco_stream_t stream);
+
+/*
+ * taco_compress with the pass structure chosen by the caller, per call:
+ *   flags          0, or TACO_FLAG_TWO_PASS: always the two kernels
+ *                  (statistics, then quantisation re-reading x), which need
+ *                  no co-residency; bitwise the same result.  Other bits:
+ *                  TACO_ERR_FLAGS.
+ *   barrier_polls  bound on the single-pass barrier's polls (0: the default,
+ *                  TACO_DEFAULT_BARRIER_POLLS); a small bound makes waits give
+ *                  up early (e.g. to exercise the timeout path in tests).
+ */
+taco_status_t taco_compress_ex(const void* x_bf16, int64_t tokens, int64_t hidden,
+                               int32_t block, float target_energy, uint8_t* q_fp8,
+                               float* alpha, float* scale, void* workspace,
+                               size_t workspace_bytes, uint32_t flags,
+                               uint32_t barrier_polls, taco_stream_t stream);
 
 /*
  * Decompress: decode -> undo s -> inverse rotation -> undo alpha -> bf16
@@ -185,7 +189,8 @@ taco_status_t taco_decompress(const uint8_t* q_fp8, const float* alpha,
  *   q_fp8, alpha, scale  HOST arrays of `nparts` DEVICE pointers (read during
  *                        the call; the arrays may be freed when it returns)
  *   nparts               1 .. TACO_MAX_PARTS
- *   out_bf16             out: bf16 [tokens, hidden]; may not alias any input
+ *   out_bf16             out: bf16 [tokens, hidden]; may not overlap any part
+ *                        (TACO_ERR_ALIAS)
  */
 taco_status_t taco_decompress_sum(const uint8_t* const* q_fp8, const float* const* alpha,
                                   const float* const* scale, int32_t nparts,
@@ -206,14 +211,14 @@ size_t taco_decompress_sum_compress_workspace_bytes(int64_t tokens, int64_t hidd
  *   Result = taco_compress(taco_decompress_sum(parts)): the bf16 sum of the
  *   parts' reconstructions (as taco_decompress_sum computes it) compressed
  *   with its own per-block alpha and per-tensor scale, bitwise equal to the
- *   two calls in sequence.  When the tensor fits on chip and single-pass mode
- *   is on (taco_set_single_pass) it is one kernel and the bf16 sum never
+ *   two calls in sequence.  When the tensor fits on chip (and TACO_FLAG_TWO_PASS
+ *   is not given to the _ex form) it is one kernel and the bf16 sum never
  *   reaches device memory; otherwise the sum goes through the workspace.
  *   q_fp8, alpha, scale   HOST arrays of `nparts` DEVICE pointers (1 ..
  *                         TACO_MAX_PARTS), as taco_decompress_sum
  *   target_energy         as taco_compress
- *   q_out, alpha_out, scale_out  out, as taco_compress; none may be one of
- *                         the inputs (TACO_ERR_ALIAS)
+ *   q_out, alpha_out, scale_out  out, as taco_compress; none may overlap an
+ *                         input, another output or the workspace (TACO_ERR_ALIAS)
  *   workspace             at least taco_decompress_sum_compress_workspace_bytes(),
  *                         256-byte aligned, zero-filled once; same ordering and
  *                         residency rules as the taco_compress workspace
@@ -225,6 +230,15 @@ taco_status_t taco_decompress_sum_compress(const uint8_t* const* q_fp8, const fl
                                            float* alpha_out, float* scale_out,
                                            void* workspace, size_t workspace_bytes,
                                            taco_stream_t stream);
+/* The same with flags and barrier_polls as in taco_compress_ex. */
+taco_status_t taco_decompress_sum_compress_ex(const uint8_t* const* q_fp8, const float* const* alpha,
+                                              const float* const* scale, int32_t nparts,
+                                              int64_t tokens, int64_t hidden, int32_t block,
+                                              float target_energy, uint8_t* q_out,
+                                              float* alpha_out, float* scale_out,
+                                              void* workspace, size_t workspace_bytes,
+                                              uint32_t flags, uint32_t barrier_polls,
+                                              taco_stream_t stream);
 
 /*
  * Single-pass Dual-Scale variants [TACO pt-summary, sections 2.B.2 (two scales
@@ -258,7 +272,7 @@ taco_status_t taco_decompress_blockscale(const uint8_t* q_fp8, const float* alph
  *   amax_out   in/out: device, TACO_AMAX_FLOATS fp32; each slot becomes the
  *                   max of its content and part of this tensor's block maxima,
  *                   so zero-filled on entry it holds this tensor's largest |y|
- *                   as the max over the buffer.  May not be amax_prev
+ *                   as the max over the buffer.  May not overlap amax_prev
  *                   (TACO_ERR_ALIAS).
  */
 taco_status_t taco_compress_delayed(const void* x_bf16, int64_t tokens, int64_t hidden,
@@ -273,10 +287,12 @@ taco_status_t taco_compress_delayed(const void* x_bf16, int64_t tokens, int64_t 
  * no rotation.  The pages give no INT8 arithmetic; this library uses
  *   A     = max |x| over the tensor (block == 0) or over each block of
  *           `block` consecutive elements of a row (block in {64, 128, 256})
- *   s     = fp32(127 / A), 1 if A == 0
- *   code  = clamp(round_half_even(fp32(x * s)), -127, 127)
- *   x_hat = bf16_RNE(fp32(code * fp32(1 / s)))
- * with every product and quotient rounded to fp32 once.
+ *   s     = fp32(127 / A), 1 if A == 0  (correctly rounded quotient)
+ *   code  = clamp(round_half_even(x * s), -127, 127)
+ *   x_hat = bf16_RNE(code / s)
+ * where x * s and code / s are the exact product and quotient: each code and
+ * each bf16 output is the correctly rounded value, decided without an fp32
+ * intermediate rounding.
  *
  *   x_bf16     in : bf16 [tokens, hidden], 16-byte aligned; hidden % 8 == 0
  *                   when block == 0, hidden % block == 0 otherwise
