@@ -12,17 +12,26 @@ once before timing, as the peers would do on their own GPUs).
 Inputs are resident in HBM when timing starts.  To keep the timed traffic in
 HBM rather than the 256 MB Infinity Cache, the step rotates over R complete
 buffer sets (16 by default, 4.3 GB together: even the op with the smallest
-inputs, decompress, reads 2 x 16 x 16.8 MB per rotation, twice the cache).  `value` is bf16 bytes moved by the calls
-(bf16 in for compress, bf16 out for the decompressions) per second.
+inputs, decompress, reads 2 x 16 x 16.8 MB per rotation, twice the cache).
+`value` is bf16 bytes moved by the calls (bf16 in for compress, bf16 out for
+the decompressions) per second.
 
 Steps are launched as HIP graphs, so the timed region measures the GPU rather
 than the host's per-call enqueue cost: one graph holds one step per buffer set
 (R steps, replayed K // R times; any remaining steps replay single-step
 graphs), because consecutive graph launches leave a gap of several
 microseconds on the GPU that one launch per step would add to every step.
-Every step still does all of its work.  The per-op durations (and the roofline
-of the compress kernels) come from their own timed regions: graphs of
-back-to-back calls of one op, OP_PASSES passes over every buffer set.
+Every step still does all of its work.  Per op:
+  * avg_us: graphs of back-to-back calls of that op, OP_PASSES passes over
+    every buffer set, timed with HIP events on the launch stream (the
+    roofline figure of the compress kernel);
+  * percall_us: median, p10 and p90 of PERCALL_CALLS cold calls (eager
+    launches over the rotating buffer sets), from the kernel durations the
+    GPU reports to torch.profiler (a call's kernels summed).
+The other workload shapes (tiny, GPT-2-1.5B, Qwen-7B) are timed the same way
+under `configs`.  The oracle's CPU baseline runs first, before the GPU is
+touched: one process (BLAS on 1 thread), and a process pool over row chunks
+on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -41,10 +50,11 @@ sys.path.insert(0, ROOT)
 METRIC = "compress/decompress GB/s (bf16 in) and % of MI355X HBM peak, 1 GPU"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
-WORKLOAD = "gpt3_6p7b"
 TOKENS, HIDDEN, BLOCK, NPARTS = 4096, 4096, 128, 4
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "compress_gpt3_6p7b_counters.json")
 OP_PASSES = 2                    # passes over the buffer sets per per-op graph
+PERCALL_CALLS = 32               # cold calls per op for the per-call statistics
+MAX_CPU_WORKERS = 16             # the host CPU share of one GPU on the measuring boxes
 
 
 def parse():
@@ -58,17 +68,24 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=TOKENS,
                    help="rows of the workload the oracle is timed on (cpu_baseline)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="the oracle's step is repeated until at least this much CPU time")
+                   help="each oracle leg repeats the step until at least this much time")
+    p.add_argument("--cpu-workers", type=int, default=0,
+                   help="processes of the all-cores oracle leg (0: the host's CPUs, at most 16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--single-pass", choices=["on", "off"], default="on",
                    help="fused single-pass compress when the tensor fits (default) or the two-kernel path")
-    p.add_argument("--all-configs", action="store_true",
-                   help="also time cold compress and decompress on the other workload shapes "
-                        "(tiny, GPT-2-1.5B, Qwen-7B; reported under 'configs', not the metric)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the other workload shapes (tiny, GPT-2-1.5B, Qwen-7B) under 'configs'")
+    p.add_argument("--no-percall", action="store_true",
+                   help="skip the per-call cold statistics (torch.profiler)")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="before timing, run 8 plain device copies of this many MiB (a known-size "
                         "kernel that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE in the same process)")
     return p.parse_args()
+
+
+def progress(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def kernel_source_hash() -> str:
@@ -92,11 +109,10 @@ def measured_counters():
     return c
 
 
-def cpu_baseline(rows: int, min_seconds: float):
-    """The oracle, as it is, on the first `rows` rows of the same step (1 BLAS
-    thread), repeated until at least `min_seconds` of CPU work."""
-    from threadpoolctl import threadpool_limits
-
+# ------------------------------------------------------------------ CPU baseline
+def _cpu_inputs(rows: int):
+    """The step's inputs on the first `rows` rows (bf16 bit patterns), and the 4
+    decompress-sum parts compressed by the oracle (untimed)."""
     import oracle
     from fp8_compression_tensor_taco_amd import workloads as W
 
@@ -104,6 +120,16 @@ def cpu_baseline(rows: int, min_seconds: float):
     grad = W.bf16_bits(W.make("gpt3_6p7b_grad", seed=1, tokens=rows))
     parts = [oracle.compress(W.bf16_bits(W.make("gpt3_6p7b_act", seed=10 + p, tokens=rows)), BLOCK)
              for p in range(NPARTS)]
+    return act, grad, parts
+
+
+def _oracle_steps(act, grad, parts, min_seconds: float):
+    """The oracle's step (compress + decompress of act and grad, decompress_sum
+    of the parts), repeated until at least min_seconds; returns (runs, seconds)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
     runs = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
@@ -115,17 +141,90 @@ def cpu_baseline(rows: int, min_seconds: float):
             runs += 1
             dt = time.perf_counter() - t0
             if dt >= min_seconds:
-                break
-    nbytes = 2 * rows * HIDDEN * 5 * runs        # bf16 bytes of the 5 calls per step
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{runs} step(s) on rows 0..{rows - 1} of the [{TOKENS},{HIDDEN}] workload "
-                      f"({rows}x{HIDDEN} per tensor; the 4 decompress-sum parts compressed beforehand), "
-                      f"numpy fp64, BLAS limited to 1 thread, {dt:.1f} s"}
+                return runs, dt
 
 
-def time_configs(taco, W, dev, stream, capture, time_us):
-    """Cold per-call compress and decompress on the other workload shapes: graphs
-    of back-to-back calls over enough buffer sets to exceed 1 GiB (at most 512)."""
+def _worker(task):
+    act, grad, parts, secs = task
+    return _oracle_steps(act, grad, parts, secs)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(rows: int, min_seconds: float, workers: int):
+    """The oracle as it is: (1) one process, BLAS on 1 thread, on the first
+    `rows` rows of the step; (2) the same step split into row chunks over a
+    pool of `workers` processes (spawned: nothing of this process is shared),
+    each chunk's step repeated for min_seconds; the step takes as long as its
+    slowest chunk, which gives the all-cores figure."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    act, grad, parts = _cpu_inputs(rows)
+    runs, dt = _oracle_steps(act, grad, parts, min_seconds)
+    step_bytes = 2 * rows * HIDDEN * 5                 # bf16 bytes of the 5 calls per step
+    single = {"value": round(step_bytes * runs / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+              "sample": f"{runs} step(s) on rows 0..{rows - 1} of the [{TOKENS},{HIDDEN}] workload, "
+                        f"{dt:.1f} s"}
+    chunks = [c for c in np.array_split(np.arange(rows), max(1, min(workers, rows))) if len(c)]
+    tasks = [(act[c[0]:c[-1] + 1], grad[c[0]:c[-1] + 1],
+              [(q[c[0]:c[-1] + 1], a[c[0]:c[-1] + 1], s) for q, a, s in parts], min_seconds)
+             for c in chunks]
+    with mp.get_context("spawn").Pool(len(tasks)) as pool:
+        res = pool.map(_worker, tasks)
+    per_step = max(t / r for r, t in res)              # seconds per step of the slowest chunk
+    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": len(tasks),
+            "kind": "oracle",
+            "sample": f"the [{TOKENS},{HIDDEN}] step (rows 0..{rows - 1}; the 4 decompress-sum parts "
+                      f"compressed beforehand) split into {len(tasks)} row chunks, one per process, each "
+                      f"chunk's step repeated for >= {min_seconds:g} s; numpy fp64, BLAS on 1 thread per "
+                      f"process; the slowest process sets the step time",
+            "nproc": os.cpu_count(), "cpus_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "single_core": single}
+
+
+# ------------------------------------------------------------------ GPU timing helpers
+def percall_stats(torch, calls):
+    """Median, p10, p90 (us) of the calls' kernel durations as the GPU reports
+    them to torch.profiler; a call that launches k kernels is the sum of its k."""
+    import numpy as np
+    from torch.profiler import ProfilerActivity, profile
+
+    torch.cuda.synchronize()
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+    ev = []
+    for e in prof.events():
+        d = getattr(e, "device_time", None)
+        if d is None:
+            d = getattr(e, "cuda_time", 0.0)
+        if d and "(anonymous namespace)::" in e.name and "_kernel" in e.name:
+            ev.append((e.time_range.start, d))
+    ev.sort()
+    if not ev or len(ev) % len(calls):
+        return {"error": f"{len(ev)} kernels for {len(calls)} calls"}
+    k = len(ev) // len(calls)
+    per = np.array([sum(d for _, d in ev[i:i + k]) for i in range(0, len(ev), k)], dtype=float)
+    return {"median": round(float(np.median(per)), 3), "p10": round(float(np.percentile(per, 10)), 3),
+            "p90": round(float(np.percentile(per, 90)), 3), "n": int(per.size), "kernels_per_call": k}
+
+
+def time_configs(taco, W, dev, capture, time_us, single_pass, percall):
+    """Cold per-call compress and decompress on the other workload shapes:
+    graphs of back-to-back calls over enough buffer sets to exceed 1 GiB (at
+    most 512), and the per-call statistics over the same sets."""
     import torch
 
     res = {}
@@ -142,24 +241,37 @@ def time_configs(taco, W, dev, stream, capture, time_us):
                  "y": torch.empty((T, H), dtype=torch.bfloat16, device=dev)} for _ in range(nsets)]
         del x0
         ws = torch.zeros(taco.workspace_bytes(T, H, B), dtype=torch.uint8, device=dev)
+
+        def comp(st):
+            taco.compress(st["x"], B, q=st["q"], alpha=st["a"], scale=st["s"], workspace=ws,
+                          single_pass=single_pass)
+
+        def dec(st):
+            taco.decompress(st["q"], st["a"], st["s"], B, out=st["y"])
+
         for st in sets:
-            taco.compress(st["x"], B, q=st["q"], alpha=st["a"], scale=st["s"], workspace=ws)
+            comp(st)
         torch.cuda.synchronize()
-        gc = capture(lambda: [taco.compress(st["x"], B, q=st["q"], alpha=st["a"], scale=st["s"], workspace=ws)
-                              for st in sets])
-        gd = capture(lambda: [taco.decompress(st["q"], st["a"], st["s"], B, out=st["y"]) for st in sets])
+        gc = capture(lambda: [comp(st) for st in sets])
+        gd = capture(lambda: [dec(st) for st in sets])
         gc.replay()
         gd.replay()
         alg = 3 * n + 4 * n // B + 4
         c_us = time_us(gc.replay, nsets, 4)
         d_us = time_us(gd.replay, nsets, 4)
-        res[name] = {"shape": [T, H], "block": B, "buffer_sets": nsets,
-                     "single_pass": bool(taco.is_single_pass(T, H, B)),
-                     "compress_us": round(c_us, 3), "decompress_us": round(d_us, 3),
-                     "compress_bf16_GBps": round(2 * n / (c_us * 1e-6) / 1e9, 1),
-                     "decompress_bf16_GBps": round(2 * n / (d_us * 1e-6) / 1e9, 1),
-                     "compress_hbm_frac": round(alg / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "decompress_hbm_frac": round(alg / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        r = {"shape": [T, H], "block": B, "buffer_sets": nsets,
+             "single_pass": bool(single_pass and taco.is_single_pass(T, H, B)),
+             "compress_us": round(c_us, 3), "decompress_us": round(d_us, 3),
+             "compress_bf16_GBps": round(2 * n / (c_us * 1e-6) / 1e9, 1),
+             "decompress_bf16_GBps": round(2 * n / (d_us * 1e-6) / 1e9, 1),
+             "compress_hbm_frac": round(alg / (c_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+             "decompress_hbm_frac": round(alg / (d_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if percall:
+            pick = [sets[(i * nsets) // PERCALL_CALLS] for i in range(PERCALL_CALLS)] \
+                if nsets >= PERCALL_CALLS else [sets[i % nsets] for i in range(PERCALL_CALLS)]
+            r["compress_percall_us"] = percall_stats(torch, [lambda st=st: comp(st) for st in pick])
+            r["decompress_percall_us"] = percall_stats(torch, [lambda st=st: dec(st) for st in pick])
+        res[name] = r
         del gc, gd, sets, ws
         torch.cuda.synchronize()
     return res
@@ -173,6 +285,13 @@ def main():
               f"has no multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE={world}).",
               file=sys.stderr)
         sys.exit(2)
+
+    # the oracle's CPU baseline first, while nothing has touched the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(MAX_CPU_WORKERS, len(os.sched_getaffinity(0)))
+        progress(f"oracle CPU baseline: 1 process, then {workers}")
+        cpu = cpu_baseline(args.cpu_rows, args.cpu_seconds, workers)
 
     import torch
     import fp8_compression_tensor_taco_amd as taco
@@ -213,7 +332,7 @@ def main():
     ws_rs = torch.zeros(taco.load().taco_decompress_sum_compress_workspace_bytes(TOKENS, HIDDEN, BLOCK),
                         dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    taco.set_single_pass(args.single_pass == "on")
+    SP = args.single_pass == "on"
     if args.copy_probe_mib > 0:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -229,12 +348,12 @@ def main():
 
     def op_compress(st, k):
         x = st["act"] if k == 0 else st["grad"]
-        taco.compress(x, BLOCK, q=st["q"][k], alpha=st["a"][k], scale=st["s"][k], workspace=ws)
+        taco.compress(x, BLOCK, q=st["q"][k], alpha=st["a"][k], scale=st["s"][k], workspace=ws, single_pass=SP)
 
     def op_decompress(st, k):
         taco.decompress(st["q"][k], st["a"][k], st["s"][k], BLOCK, out=st["xh"][k])
 
-    def op_sum(st):
+    def op_sum(st, k=0):
         taco.decompress_sum(st["parts"], BLOCK, out=st["sum"])
 
     amax = [torch.zeros(taco.TACO_AMAX_FLOATS, dtype=torch.float32, device=dev) for _ in range(2)]
@@ -260,9 +379,9 @@ def main():
         taco.decompress_int8(st["q"][k].view(torch.int8), st["s"][k] if block == 0 else st["sblk"], block,
                              out=st["xh"][k])
 
-    def op_sum_compress(st):
+    def op_sum_compress(st, k=0):
         taco.decompress_sum_compress(st["parts"], BLOCK, q=st["rq"], alpha=st["ra"], scale=st["rs"],
-                                     workspace=ws_rs)
+                                     workspace=ws_rs, single_pass=SP)
 
     def step(st):
         for k in range(2):
@@ -285,29 +404,20 @@ def main():
     step_graphs = [capture(lambda st=st: step(st)) for st in sets]
     cycle_graph = capture(lambda: [step(st) for st in sets])
     P = OP_PASSES
-    op_graphs = {
-        "compress": (capture(lambda: [op_compress(st, k) for _ in range(P) for st in sets for k in range(2)]),
-                     2 * P * len(sets)),
-        "decompress": (capture(lambda: [op_decompress(st, k) for _ in range(P) for st in sets for k in range(2)]),
-                       2 * P * len(sets)),
-        "decompress_sum": (capture(lambda: [op_sum(st) for _ in range(P) for st in sets]), P * len(sets)),
-        "decompress_sum_compress": (capture(lambda: [op_sum_compress(st) for _ in range(P) for st in sets]),
-                                    P * len(sets)),
-        "compress_blockscale": (capture(lambda: [op_blockscale(st, k) for _ in range(P) for st in sets
-                                                 for k in range(2)]), 2 * P * len(sets)),
-        "decompress_blockscale": (capture(lambda: [op_blockscale_dec(st, k) for _ in range(P) for st in sets
-                                                   for k in range(2)]), 2 * P * len(sets)),
-        "compress_delayed": (capture(lambda: [op_delayed(st, k) for _ in range(P) for st in sets
-                                              for k in range(2)]), 2 * P * len(sets)),
-        "compress_int8_tensor": (capture(lambda: [op_int8(st, k, 0) for _ in range(P) for st in sets
-                                                  for k in range(2)]), 2 * P * len(sets)),
-        "decompress_int8_tensor": (capture(lambda: [op_int8_dec(st, k, 0) for _ in range(P) for st in sets
-                                                    for k in range(2)]), 2 * P * len(sets)),
-        "compress_int8_block": (capture(lambda: [op_int8(st, k, BLOCK) for _ in range(P) for st in sets
-                                                 for k in range(2)]), 2 * P * len(sets)),
-        "decompress_int8_block": (capture(lambda: [op_int8_dec(st, k, BLOCK) for _ in range(P) for st in sets
-                                                   for k in range(2)]), 2 * P * len(sets)),
+    # op -> (function of (set, k), calls per set)
+    op_fns = {
+        "compress": (op_compress, 2), "decompress": (op_decompress, 2), "decompress_sum": (op_sum, 1),
+        "decompress_sum_compress": (op_sum_compress, 1),
+        "compress_blockscale": (op_blockscale, 2), "decompress_blockscale": (op_blockscale_dec, 2),
+        "compress_delayed": (op_delayed, 2),
+        "compress_int8_tensor": (lambda st, k: op_int8(st, k, 0), 2),
+        "decompress_int8_tensor": (lambda st, k: op_int8_dec(st, k, 0), 2),
+        "compress_int8_block": (lambda st, k: op_int8(st, k, BLOCK), 2),
+        "decompress_int8_block": (lambda st, k: op_int8_dec(st, k, BLOCK), 2),
     }
+    op_graphs = {op: (capture(lambda f=f, nk=nk: [f(st, k) for _ in range(P) for st in sets for k in range(nk)]),
+                      nk * P * len(sets))
+                 for op, (f, nk) in op_fns.items()}
     cycle_graph.replay()
     for g in step_graphs:
         g.replay()
@@ -315,6 +425,7 @@ def main():
         g.replay()
     torch.cuda.synchronize()
 
+    progress("graphs captured; timed steps")
     # ---- timed region: K steps (graph replays) bracketed by events on the launch stream
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -334,8 +445,8 @@ def main():
     # ---- per-op timed regions: average duration of one call of each op
     reps = max(1, args.steps // (4 * OP_PASSES))
     avg_us = {}
-    extra = ["decompress_sum_compress", "compress_blockscale", "decompress_blockscale", "compress_delayed",
-             "compress_int8_tensor", "decompress_int8_tensor", "compress_int8_block", "decompress_int8_block"]
+    extra = [op for op in op_fns if op not in ops]
+
     def time_us(fn, calls, repeat):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -350,6 +461,15 @@ def main():
     for op in ops + extra:
         g, calls = op_graphs[op]
         avg_us[op] = time_us(g.replay, calls, reps)
+    del op_graphs, step_graphs, cycle_graph
+
+    # ---- per-call cold statistics: eager calls over the rotating sets
+    progress("per-op averages done; per-call statistics")
+    percall = {}
+    if not args.no_percall:
+        for op, (f, nk) in op_fns.items():
+            calls = [lambda f=f, st=sets[(i // nk) % len(sets)], k=i % nk: f(st, k) for i in range(PERCALL_CALLS)]
+            percall[op] = percall_stats(torch, calls)
 
     # ---- warm: the step's ops back to back on one buffer set, whose inputs stay
     # in the 256 MB Infinity Cache (reported apart, labeled; not the metric)
@@ -383,8 +503,17 @@ def main():
     g5 = capture(layers)
     g5.replay()
     graph_us = time_us(g5.replay, L5, 3)
+    percall5 = None if args.no_percall else percall_stats(
+        torch, [lambda layer=layer: taco.decompress_sum(slots5[layer], B5, out=outs5[layer]) for layer in range(L5)])
     del g5, slots5, outs5
     torch.cuda.empty_cache()
+
+    configs = None
+    if not args.no_configs:
+        progress("other workload shapes")
+        del sets
+        torch.cuda.empty_cache()
+        configs = time_configs(taco, W, dev, capture, time_us, SP, not args.no_percall)
 
     N = TOKENS * HIDDEN
     bf16_bytes_step = 2 * N * 5
@@ -417,6 +546,16 @@ def main():
                 "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
                 "frac": round(executed / MFMA_BF16_PEAK_TFLOPS, 4)}
 
+    def op_entry(op, with_bf16):
+        e = {"avg_us": round(avg_us[op], 3)}
+        if with_bf16:
+            e["bf16_GBps"] = round(2 * N / (avg_us[op] * 1e-6) / 1e9, 1)
+        e["algorithmic_GBps"] = round(alg[op] / (avg_us[op] * 1e-6) / 1e9, 1)
+        e["hbm_frac"] = round(alg[op] / (avg_us[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        if op in percall:
+            e["percall_us"] = percall[op]
+        return e
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -440,7 +579,7 @@ def main():
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
-            "kernel": ("compress_fused_lds_kernel (single pass)" if taco.get_single_pass()
+            "kernel": ("compress_fused_lds_kernel (single pass)" if SP
                        else "compress_stats_mfma_kernel + compress_quant_mfma_kernel"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
@@ -452,19 +591,8 @@ def main():
             "avg_us": round(avg_us["compress"], 3),
             "mfma": mfma,
         },
-        "ops": {
-            op: {"avg_us": round(avg_us[op], 3),
-                 "bf16_GBps": round(2 * N / (avg_us[op] * 1e-6) / 1e9, 1),
-                 "algorithmic_GBps": round(alg[op] / (avg_us[op] * 1e-6) / 1e9, 1),
-                 "hbm_frac": round(alg[op] / (avg_us[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-            for op in ops
-        },
-        "extra_ops": {
-            op: {"avg_us": round(avg_us[op], 3),
-                 "algorithmic_GBps": round(alg[op] / (avg_us[op] * 1e-6) / 1e9, 1),
-                 "hbm_frac": round(alg[op] / (avg_us[op] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-            for op in extra
-        },
+        "ops": {op: op_entry(op, True) for op in ops},
+        "extra_ops": {op: op_entry(op, False) for op in extra},
         "extra_ops_note": "not part of the step: decompress_sum_compress (4 parts -> FP8 of their bf16 "
                           "sum), the per-block-guard and delayed-scale Dual-Scale variants, and the INT8 "
                           "degrade path (absmax per tensor: two kernels, x read twice; per 128-block)",
@@ -476,15 +604,17 @@ def main():
             "us_per_layer_eager_launches": round(eager_us, 3),
             "us_per_layer_one_graph": round(graph_us, 3),
             "launch_gap_us_per_layer": round(eager_us - graph_us, 3),
+            "percall_us": percall5,
             "algorithmic_GBps_one_graph": round((NPARTS * (N + 4 * (N // B5) + 4) + 2 * N) / (graph_us * 1e-6) / 1e9, 1)},
         "wall_s_timed": round(t_wall, 4),
-        "timing": "steps replayed as HIP graphs of one step per buffer set (each step all 5 calls); per-op "
-                  f"figures from graphs of back-to-back calls, {OP_PASSES} passes over all buffer sets",
+        "timing": "steps replayed as HIP graphs of one step per buffer set (each step all 5 calls); avg_us "
+                  f"from graphs of back-to-back calls, {OP_PASSES} passes over all buffer sets; percall_us: "
+                  f"median/p10/p90 of {PERCALL_CALLS} cold eager calls, kernel durations from torch.profiler",
     }
-    if args.all_configs:
-        out["configs"] = time_configs(taco, W, dev, stream, capture, time_us)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_rows, args.cpu_seconds)
+    if configs is not None:
+        out["configs"] = configs
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

@@ -29,5 +29,6 @@ def test_world_size_above_one_is_refused():
 def test_help_lists_the_options():
     r = run("--help")
     assert r.returncode == 0
-    for opt in ("--gpus", "--steps", "--warmup", "--rotate", "--all-configs", "--no-cpu-baseline"):
+    for opt in ("--gpus", "--steps", "--warmup", "--rotate", "--no-configs", "--no-percall", "--no-cpu-baseline",
+                "--cpu-workers"):
         assert opt in r.stdout
