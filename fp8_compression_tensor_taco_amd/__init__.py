@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     compress_blockscale,
     compress_delayed,
     compress_int8,
+    compress_noalloc,
     TACO_DEFAULT_BARRIER_POLLS,
     TACO_FLAG_TWO_PASS,
     is_single_pass,
@@ -32,7 +33,7 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "TACO_AMAX_FLOATS", "TACO_AMAX_SLOTS", "TACO_DEFAULT_BARRIER_POLLS", "TACO_FLAG_TWO_PASS", "TACO_MAX_PARTS",
-    "TacoError", "compress", "compress_blockscale", "compress_delayed", "compress_int8", "decompress",
+    "TacoError", "compress", "compress_blockscale", "compress_delayed", "compress_int8", "compress_noalloc", "decompress",
     "decompress_blockscale", "decompress_int8", "decompress_sum", "decompress_sum_compress", "is_single_pass",
     "library_path", "load", "num_scales", "two_shot_allreduce", "version", "workspace_bytes",
     "workspace_timed_out",

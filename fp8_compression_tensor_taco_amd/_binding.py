@@ -80,6 +80,9 @@ def load() -> ctypes.CDLL:
         lib.taco_compress_ex.restype = ctypes.c_int
         lib.taco_compress_ex.argtypes = [_vp, _i64, _i64, _i32, ctypes.c_float, _vp, _vp, _vp,
                                          _vp, ctypes.c_size_t, _u32, _u32, _vp]
+        lib.taco_compress_noalloc.restype = ctypes.c_int
+        lib.taco_compress_noalloc.argtypes = [_vp, _i64, _i64, _i32, ctypes.c_float, _vp, _vp, _vp,
+                                              _u32, _u32, _vp]
         lib.taco_decompress.restype = ctypes.c_int
         lib.taco_decompress.argtypes = [_vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp]
         lib.taco_decompress_sum_compress_workspace_bytes.restype = ctypes.c_size_t
@@ -288,6 +291,30 @@ def _compress(x, block, target_energy, q, alpha, scale, workspace, stream, singl
     _check(lib.taco_compress_ex(*args, flags, polls, handle))
     if check_barrier and flags == 0 and _timed_out_and_clear(lib, workspace, handle):
         _check(lib.taco_compress_ex(*args, TACO_FLAG_TWO_PASS, polls, handle))
+    return q, alpha, scale
+
+
+def compress_noalloc(x: torch.Tensor, block: int, target_energy: float = 1.0, *, q: torch.Tensor,
+                     alpha: torch.Tensor, scale: torch.Tensor, stream=None, single_pass: bool = True,
+                     barrier_polls: int = 0):
+    """compress() with the workspace in the library's own device scratch
+    (taco_compress_noalloc): neither the library nor this function allocates,
+    so the outputs must be passed in.  Calls on one GPU share the scratch and
+    must be ordered."""
+    lib = load()
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 2-D bfloat16 tensor")
+    dev = _require_gpu(x, q, alpha, scale)
+    T, H = x.shape
+    n = lib.taco_num_scales(T, H, block)
+    if n < 0:
+        _check(4 if block not in (64, 128, 256) else 3)
+    _require_buffer(q, "q", torch.uint8, T * H, (T, H))
+    _require_buffer(alpha, "alpha", torch.float32, n)
+    _require_buffer(scale, "scale", torch.float32, 1)
+    flags, polls = _pass_args(single_pass, barrier_polls)
+    _check(lib.taco_compress_noalloc(_ptr(x), T, H, block, float(target_energy), _ptr(q), _ptr(alpha),
+                                     _ptr(scale), flags, polls, _stream(dev, stream)))
     return q, alpha, scale
 
 

@@ -55,6 +55,7 @@
 #include <algorithm>
 #include <cstddef>
 #include <initializer_list>
+#include <mutex>
 
 #include "taco.h"
 
@@ -1949,6 +1950,35 @@ taco_status_t check_flags(uint32_t flags) {
 
 }  // namespace
 
+// Workspace of taco_compress_noalloc: the compress workspace (barrier state
+// and partial maxima) in device memory the library holds itself, one copy per
+// GPU until the process ends.  Static storage starts zeroed, and every call
+// leaves the barrier state ready for the next one, so nothing clears it.  In
+// host code the name stands for no device address: the kernels get the
+// address hipGetSymbolAddress returns on each device.
+static __device__ __align__(256) char scratch[kCompressWorkspace];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64] = {};
+
+// The current device's copy of `scratch` (looked up once per device), or null
+// if the lookup fails.
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 // ----------------------------------------------------------------- C ABI
 
 extern "C" {
@@ -2042,6 +2072,20 @@ taco_status_t taco_compress(const void* x_bf16, int64_t tokens, int64_t hidden, 
                             void* workspace, size_t workspace_bytes, taco_stream_t stream) {
   return taco_compress_ex(x_bf16, tokens, hidden, block, target_energy, q_fp8, alpha, scale, workspace,
                           workspace_bytes, 0, 0, stream);
+}
+
+taco_status_t taco_compress_noalloc(const void* x_bf16, int64_t tokens, int64_t hidden, int32_t block,
+                                    float target_energy, uint8_t* q_fp8, float* alpha, float* scale,
+                                    uint32_t flags, uint32_t barrier_polls, taco_stream_t stream) {
+  if (!x_bf16 || !q_fp8 || !alpha || !scale) return TACO_ERR_NULL;
+  const taco_status_t st = check_shape(tokens, hidden, block);
+  if (st != TACO_OK) return st;
+  if (taco_compress_workspace_bytes(tokens, hidden, block) > sizeof(scratch)) return TACO_ERR_WORKSPACE;
+  if (device_cu_count() <= 0) return TACO_ERR_HIP;
+  void* ws = scratch_on_current_device();
+  if (ws == nullptr) return TACO_ERR_HIP;
+  return taco_compress_ex(x_bf16, tokens, hidden, block, target_energy, q_fp8, alpha, scale, ws,
+                          sizeof(scratch), flags, barrier_polls, stream);
 }
 
 taco_status_t taco_decompress(const uint8_t* q_fp8, const float* alpha, const float* scale,

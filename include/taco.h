@@ -172,6 +172,24 @@ taco_status_t taco_compress_ex(const void* x_bf16, int64_t tokens, int64_t hidde
                                uint32_t barrier_polls, taco_stream_t stream);
 
 /*
+ * taco_compress_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the workspace is the library's own device
+ * scratch, 37120 bytes per GPU (the size taco_compress_workspace_bytes gives
+ * for every shape, so no shape is too large for it; a larger requirement would
+ * return TACO_ERR_WORKSPACE), held until the process ends.  The call allocates
+ * nothing; it looks the scratch up once per device, on the first call with that
+ * device current.  Every call on a GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (on different streams) race, so they must be ordered.
+ * Arguments, results, flags, barrier_polls and errors as taco_compress_ex;
+ * a barrier timeout gives NaN codes as there, and its flag cannot be queried.
+ */
+taco_status_t taco_compress_noalloc(const void* x_bf16, int64_t tokens, int64_t hidden,
+                                    int32_t block, float target_energy, uint8_t* q_fp8,
+                                    float* alpha, float* scale, uint32_t flags,
+                                    uint32_t barrier_polls, taco_stream_t stream);
+
+/*
  * Decompress: decode -> undo s -> inverse rotation -> undo alpha -> bf16
  * [TACO pt-summary, section 2.B.2: both scales reverse the process].
  *   q_fp8, alpha, scale  in : the output of taco_compress (same shape / block)
