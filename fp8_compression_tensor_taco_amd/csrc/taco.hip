@@ -302,6 +302,22 @@ __device__ __forceinline__ void lds_store_tile_to_global(const char* lds, uint4*
   }
 }
 
+// The wavefront's index in its workgroup, as a wave-uniform (scalar) value:
+// the compiler cannot tell that threadIdx.x / 64 is uniform, and would
+// otherwise keep every tile index derived from it in a pair of VGPRs per lane.
+__device__ __forceinline__ int wave_in_group() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
+// A wave-uniform 64-bit value moved to SGPRs.  The builtin returns int, so
+// each half goes through unsigned before it is widened: widening the int
+// itself would sign-extend the low half into the high one.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<unsigned>(v))));
+  const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<unsigned>(v >> 32))));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 __device__ __forceinline__ int rows_valid(int64_t tile, int64_t nblocks) {
   const int64_t r = nblocks - tile * kTileBlocks;
   return r >= kTileBlocks ? kTileBlocks : static_cast<int>(r);
@@ -445,7 +461,7 @@ __global__ __launch_bounds__(kThreads) void compress_stats_mfma_kernel(
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
   float amax = 0.0f;
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
+  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + wave_in_group(); t0 < ntiles;
        t0 += nw * U) {
     uint4 xr[U][NK];
 #pragma unroll
@@ -503,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void compress_quant_mfma_kernel(
   const HadFrag F = make_hadamard_fragments();
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * kWaves;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + wave_in_group();
   uint4 xr[U][NK];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -643,9 +659,7 @@ static_assert(kLeaves == 64, "arrive_wave0 advances one unused leaf per lane");
 __device__ float grid_max_wave0(float wg_max, unsigned long long leaf_count, char* __restrict__ ws,
                                 unsigned spin_limit) {
   const int lane = threadIdx.x & 63;
-  const unsigned long long v =
-      (static_cast<unsigned long long>(__builtin_amdgcn_readfirstlane(static_cast<unsigned>(leaf_count >> 32)))
-       << 32) | __builtin_amdgcn_readfirstlane(static_cast<unsigned>(leaf_count));
+  const unsigned long long v = uniform_u64(leaf_count);
   const unsigned epoch = static_cast<unsigned>((v - 1) / kLeafWgs) + 1;   // call number + 1
   if (lane == 0)
     store_agent(slot_of(ws, blockIdx.x), (static_cast<unsigned long long>(epoch) << 32) | __float_as_uint(wg_max));
@@ -688,7 +702,7 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
   const HadFrag F = make_hadamard_fragments();
   const int lane = threadIdx.x & 63, n = lane & 15;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
-  const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + (threadIdx.x >> 6);
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + wave_in_group();
   const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
   // No branch may separate these loads from their first use: the compiler
   // would wait for every outstanding load at the join.  Tiles past the end
@@ -771,19 +785,20 @@ struct LdsTile {
   static __device__ __forceinline__ int swz(int n) { return B == 64 ? (n >> 1) & 7 : n & 15; }
 };
 
-// One gfx950 direct-to-LDS copy: lane i writes the 16 bytes at g to LDS
+// One gfx950 direct-to-LDS copy: lane i writes the 16 bytes at base + off
+// (base wave-uniform, in an SGPR pair; off a per-lane byte offset) to LDS
 // address lds + 16 i (lds is wave-uniform, in m0), non-temporal like the
 // direct loads.  Written as inline asm because with the compiler's builtin it
 // waits for every copy in flight before the wavefront's first LDS read
 // (vmcnt(0)), which serialises each tile's rotation behind all of the
 // wavefront's copies; the caller waits instead with wait_copies, tile by
 // tile.  One wait state separates the write of m0 from the copy that reads
-// it.  No VGPR is written, and the address VGPRs are read at issue.  Nothing
+// it.  No VGPR is written, and the offset VGPR is read at issue.  Nothing
 // else in these kernels uses m0.
-__device__ __forceinline__ void copy16_to_lds(const uint4* g, unsigned lds) {
+__device__ __forceinline__ void copy16_to_lds(const uint4* base, unsigned off, unsigned lds) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-               :: "v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 #endif
 }
 
@@ -811,7 +826,9 @@ __device__ __forceinline__ void copy_tile_to_lds(const uint4* __restrict__ x, in
   constexpr int C16 = LdsTile<B>::C16;
   const int lane = threadIdx.x & 63;
   const int rv = rows_valid(t, nblocks);
-  const uint4* tile = x + t * (kTileBlocks * C16);
+  // t is wave-uniform, so the tile's address goes to SGPRs and each copy
+  // needs one offset VGPR (the same for every whole tile)
+  const uint4* tile = reinterpret_cast<const uint4*>(uniform_u64(reinterpret_cast<uint64_t>(x + t * (kTileBlocks * C16))));
   const unsigned base = __builtin_amdgcn_readfirstlane(
       static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_tile)));
 #pragma unroll
@@ -819,7 +836,7 @@ __device__ __forceinline__ void copy_tile_to_lds(const uint4* __restrict__ x, in
     const int pos = 64 * d + lane;
     const int n = pos / C16, p = pos % C16;
     const int row = n < rv ? n : rv - 1;
-    copy16_to_lds(tile + row * C16 + (p ^ LdsTile<B>::swz(n)), base + 1024 * d);
+    copy16_to_lds(tile, 16u * static_cast<unsigned>(row * C16 + (p ^ LdsTile<B>::swz(n))), base + 1024 * d);
   }
 }
 
@@ -847,7 +864,7 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_lds_kernel(
   const HadFrag F = make_hadamard_fragments();
   const int lane = threadIdx.x & 63, n = lane & 15;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
-  const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + (threadIdx.x >> 6);
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + wave_in_group();
   const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
   // counted into the barrier first: its add returns nothing and its load is
   // not waited for before the barrier
@@ -911,6 +928,106 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_lds_kernel(
     const float c = (al[i] * s) * Blk<B>::rsqrt_b;
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) codes_to_lds_mfma<B>(y[i][mt], c, mt, xlds);
+    __builtin_amdgcn_wave_barrier();
+    lds_store_tile_to_global<B, SROW, TACO_NT_CODE_STORES != 0>(xlds, q, t, rows_valid(t, nblocks));
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// The x-holding configurations stage x through LDS as well, in a ring of two
+// tile slots per wavefront, since a workgroup's tiles (up to 256 KiB) do not
+// fit in LDS at once: tile i + 2 is copied into tile i's slot as soon as tile
+// i has moved into registers, so two tiles per wavefront are in flight until
+// the last.  The tiles stay in registers as bf16 x across the barrier and are
+// rotated again after it, as in compress_fused_kernel, whose arithmetic per
+// tile (and so result) this is.  [8192, 3584] at B = 128, 4 tiles per
+// wavefront, cold: 23.2 us with the direct loads (21.4 us of it remained
+// with the barrier taken out, so the loads themselves were the cost), 19.8 us
+// with the ring.
+__device__ __forceinline__ void lds_reads_done() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
+template <int B, int TPW, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void compress_fused_ring_kernel(
+    const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
+    float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q, unsigned spin_limit) {
+  constexpr int NK = B / 32, NM = B / 16, SROW = Blk<B>::kCodeRowMfma, TB = LdsTile<B>::kBytes;
+  constexpr int S = 2, KC = LdsTile<B>::kCopies;
+  static_assert(WAVES * S * TB <= 128 * 1024, "the ring exceeds the LDS budget");
+  static_assert(TPW > S, "fewer tiles than slots: use compress_fused_lds_kernel");
+  static_assert(kTileBlocks * SROW <= TB, "the code tile is staged in the first slot");
+  __shared__ float red[WAVES];
+  __shared__ float amax_sh;
+  __shared__ __attribute__((aligned(1024))) char xlds_all[WAVES][S * TB];
+  char* xlds = xlds_all[threadIdx.x >> 6];
+  const HadFrag F = make_hadamard_fragments();
+  const int lane = threadIdx.x & 63, n = lane & 15;
+  const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + wave_in_group();
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
+  unsigned long long leaf = 0;
+  if (threadIdx.x < 64) leaf = arrive_wave0(ws);
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const int64_t t = wid + i * nw;
+    copy_tile_to_lds<B>(x, t < ntiles ? t : ntiles - 1, nblocks, xlds + i * TB);
+  }
+  uint4 xr[TPW][NK];
+  float al[TPW];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    const int64_t tc = t < ntiles ? t : ntiles - 1;
+    const int rv = rows_valid(tc, nblocks);
+    // tiles issued after tile i: tile i + 1 (issued at tile i - 1), unless i is the last
+    if (i + 1 < TPW) wait_copies<KC>(); else wait_copies<0>();
+    read_tile_from_lds<B>(xlds + (i % S) * TB, xr[i]);
+    if (i + S < TPW) {
+      lds_reads_done();   // the slot is free once its reads have returned
+      const int64_t tn = wid + (i + S) * nw;
+      copy_tile_to_lds<B>(x, tn < ntiles ? tn : ntiles - 1, nblocks, xlds + (i % S) * TB);
+    }
+    al[i] = ash_scale(column_sum_squares<B>(xr[i]), sqrt_eb);
+    float m = 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) {
+      const f32x4_t v = hadamard_mtile<B>(F, xr[i], mt);
+      m = fmaxf(fmaxf(m, fabsf(v[0])), fabsf(v[1]));
+      m = fmaxf(fmaxf(m, fabsf(v[2])), fabsf(v[3]));
+    }
+    if (t < ntiles && n < rv) amax = fmaxf(amax, m * (al[i] * Blk<B>::rsqrt_b));
+  }
+  // alpha after every tile's copies (a store in flight would count in the
+  // waits above)
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    const int64_t tc = t < ntiles ? t : ntiles - 1;
+    const int rv = rows_valid(tc, nblocks);
+    alpha[tc * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
+  }
+  const float wg = workgroup_max<WAVES>(amax, red);
+  if (threadIdx.x < 64) {
+    const float A = grid_max_wave0(wg, leaf, ws, spin_limit);
+    if (threadIdx.x == 0) amax_sh = A;
+  }
+  __syncthreads();
+  const float A = amax_sh;
+  const float s = A == 0.0f ? 1.0f : kQmax / A;   // NaN stays NaN
+  if (blockIdx.x == 0 && threadIdx.x == 0) *scale = s;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int64_t t = wid + i * nw;
+    if (t >= ntiles) continue;
+    const float c = (al[i] * s) * Blk<B>::rsqrt_b;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) codes_to_lds_mfma<B>(hadamard_mtile<B>(F, xr[i], mt), c, mt, xlds);
     __builtin_amdgcn_wave_barrier();
     lds_store_tile_to_global<B, SROW, TACO_NT_CODE_STORES != 0>(xlds, q, t, rows_valid(t, nblocks));
     __builtin_amdgcn_wave_barrier();
@@ -1016,7 +1133,7 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
   const float s = SBLK ? 1.0f : *scale;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t0 < ntiles;
+  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + wave_in_group(); t0 < ntiles;
        t0 += W * U) {
     uint2 raw[U][NA];
     float al[U], sk[U];
@@ -1105,7 +1222,7 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
   const Quad qd;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6); t < ntiles; t += W) {
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + wave_in_group(); t < ntiles; t += W) {
     const int64_t k = t * kTileBlocks + qd.blk;
     const bool ok = k < nblocks;
     float acc[NA][8];
@@ -1171,7 +1288,7 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
   const Quad qd;
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
-  const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + (threadIdx.x >> 6);
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + wave_in_group();
   const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
   f32x4_t y[TPW][NM];
   float al[TPW];
@@ -1319,7 +1436,7 @@ __global__ __launch_bounds__(64 * WAVES) void compress_streaming_kernel(
   const HadFrag F = make_hadamard_fragments();
   const int lane = threadIdx.x & 63, n = lane & 15;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * WAVES + (threadIdx.x >> 6);
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * WAVES + wave_in_group();
   const int64_t tc = t < ntiles ? t : ntiles - 1;
   const int rv = rows_valid(tc, nblocks);
   const int row = n < rv ? n : rv - 1;
@@ -1715,6 +1832,12 @@ bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, flo
     if (g > cap) return false;
     if (launch)
       hipLaunchKernelGGL((compress_fused_lds_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
+                         stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, polls);
+  } else if constexpr (!HOLD_Y && TACO_FUSED_LDS != 0) {   // x held, staged through an LDS ring
+    static const int cap = fused_grid_cap(resident_grid(compress_fused_ring_kernel<B, TPW, WAVES>, 64 * WAVES));
+    if (g > cap) return false;
+    if (launch)
+      hipLaunchKernelGGL((compress_fused_ring_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
                          stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, polls);
   } else {
     static const int cap = fused_grid_cap(resident_grid(compress_fused_kernel<B, TPW, HOLD_Y, WAVES>, 64 * WAVES));

@@ -208,8 +208,9 @@ def test_fused_matches_two_pass_bitwise(taco):
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     # B <= 128 holding y: x staged through LDS (1, 2 and 4 tiles per wavefront,
     # the two 4095-token shapes with a ragged last tile); the last four hold the
-    # bf16 input rather than the rotated blocks (4, 3, 6 and 4 tiles per
-    # wavefront; the last with 8 wavefronts per CU)
+    # bf16 input rather than the rotated blocks, staged through a ring of two
+    # LDS tiles (4, 3, 6 and 4 tiles per wavefront; the last with 8 wavefronts
+    # per CU)
     cases = [("gpt3_6p7b_act", 4096, 128), ("tiny", 3, 64), ("gpt2_1p5b", 4096, 64),
              ("tiny", 256, 256), ("gpt3_6p7b_grad", 1024, 128), ("dsum_part", 17, 256),
              ("qwen_7b", 4096, 64), ("gpt2_1p5b", 4095, 64), ("qwen_7b", 4095, 128),
@@ -311,6 +312,63 @@ def test_barrier_timeout_fallback_gives_the_exact_result(taco):
     for r, t in zip(ref2, got2):
         assert torch.equal(r, t)
     assert not taco.workspace_timed_out(ws2)
+
+
+# The barrier's workspace layout, as the kernels define it: a 256-byte root
+# line (the timed-out flag at byte 8), 64 leaf lines of 256 bytes whose first
+# 8 bytes are a running count, 1024 partial maxima of 4 bytes, then 1024 slots
+# of 16 bytes whose first 8 hold (epoch << 32) | max bits.
+LEAF0, LINE, LEAVES = 256, 256, 64
+SLOT0, SLOT_STRIDE, SLOTS = 256 * 65 + 4 * 1024, 16, 1024
+
+
+def _preset_barrier(ws, calls):
+    """Writes the barrier state that `calls` calls leave: every leaf count at
+    16 * calls and every slot at epoch `calls` (its low 32 bits)."""
+    w = ws[:SLOT0 + SLOT_STRIDE * SLOTS].cpu().numpy().copy()
+    for l in range(LEAVES):
+        w[LEAF0 + LINE * l:LEAF0 + LINE * l + 8].view(np.uint64)[0] = np.uint64(16 * calls)
+    slots = w[SLOT0:].view(np.uint64).reshape(SLOTS, 2)
+    slots[:, 0] = np.uint64((calls & 0xFFFFFFFF) << 32)
+    ws[:w.size].copy_(torch.from_numpy(w))
+
+
+@pytest.mark.parametrize("calls", [(1 << 27) - 1, (1 << 28) - 1])
+def test_barrier_counts_cross_bit_31_and_bit_32(taco, calls):
+    """The leaf counts are 64-bit and never reset.  From the state after
+    2^27 - 1 (2^28 - 1) calls, the next call takes the low word of the counts
+    across 2^31 (2^32) and the later ones run beyond it: every workgroup
+    still derives the same epoch from its count, so no poll gives up and
+    the results equal a fresh workspace's, for a kernel holding y, one
+    holding x and the fused decompress-sum-compress.  (The count was once
+    widened from a signed 32-bit half, which gave the workgroups that read a
+    count with bit 31 set another epoch.)"""
+    block = 128
+    for name, tokens, hidden in [("gpt3_6p7b_act", 4096, 4096), ("qwen_7b", 8192, 3584)]:
+        x = W.make(name, seed=31, tokens=tokens).cuda()
+        assert taco.is_single_pass(tokens, hidden, block)
+        ref = _compress_with(taco, x, block, True, torch.zeros(taco.workspace_bytes(tokens, hidden, block),
+                                                                dtype=torch.uint8, device="cuda"))
+        ws = torch.zeros(taco.workspace_bytes(tokens, hidden, block), dtype=torch.uint8, device="cuda")
+        _preset_barrier(ws, calls)
+        for k in range(3):
+            print(f"[case] {name} compress, call {calls + k} of a preset workspace", flush=True)
+            for r, t in zip(ref, _compress_with(taco, x, block, True, ws)):
+                assert torch.equal(r, t)
+            assert not taco.workspace_timed_out(ws)
+    parts = [tuple(t.clone() for t in taco.compress(W.make("gpt3_6p7b_act", seed=60 + i, tokens=4096).cuda(),
+                                                     block)) for i in range(2)]
+    nbytes = taco.load().taco_decompress_sum_compress_workspace_bytes(4096, 4096, block)
+    ref2 = [t.clone() for t in taco.decompress_sum_compress(
+        parts, block, workspace=torch.zeros(nbytes, dtype=torch.uint8, device="cuda"))]
+    ws2 = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    _preset_barrier(ws2, calls)
+    for k in range(3):
+        print(f"[case] decompress-sum-compress, call {calls + k} of a preset workspace", flush=True)
+        got = [t.clone() for t in taco.decompress_sum_compress(parts, block, workspace=ws2)]
+        for r, t in zip(ref2, got):
+            assert torch.equal(r, t)
+        assert not taco.workspace_timed_out(ws2)
 
 
 def test_determinism(engine):
