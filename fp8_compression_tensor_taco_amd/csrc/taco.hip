@@ -1290,6 +1290,10 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + wave_in_group();
   const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
+  // counted into the barrier first: its add returns nothing and its load is
+  // not waited for before the barrier
+  unsigned long long leaf = 0;
+  if (threadIdx.x < 64) leaf = arrive_wave0(ws);
   f32x4_t y[TPW][NM];
   float al[TPW];
   float amax = 0.0f;
@@ -1368,9 +1372,6 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
   }
   const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x < 64) {
-    // counted here rather than at the start: a leaf count held across the
-    // parts' accumulation made the allocator spill (B = 128, 2 tiles)
-    const unsigned long long leaf = arrive_wave0(ws);
     const float A = grid_max_wave0(wg, leaf, ws, spin_limit);
     if (threadIdx.x == 0) amax_sh = A;
   }
