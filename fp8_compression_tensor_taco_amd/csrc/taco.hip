@@ -653,9 +653,40 @@ __device__ __forceinline__ unsigned long long arrive_wave0(char* __restrict__ ws
 }
 static_assert(kLeaves == 64, "arrive_wave0 advances one unused leaf per lane");
 
+// One round of polls for grids of at most 256 workgroups: this lane's 4
+// slots (slot 0, which this call writes too, stands in past the grid).
+__device__ __forceinline__ void poll_round(char* __restrict__ ws, unsigned lane, unsigned long long (&r)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const unsigned j = lane + 64 * k;
+    r[k] = load_agent(slot_of(ws, j < gridDim.x ? j : 0));
+  }
+}
+
+// Whether every slot of a round carries the epoch; m gets the round's max.
+__device__ __forceinline__ bool round_ready(const unsigned long long (&r)[4], unsigned epoch, unsigned& m) {
+  bool ok = true;
+  unsigned mm = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    ok = ok && static_cast<unsigned>(r[k] >> 32) == epoch;
+    mm = max(mm, static_cast<unsigned>(r[k]));
+  }
+  m = mm;
+  return __builtin_amdgcn_ballot_w64(!ok) == 0;
+}
+
 // Grid-wide max; called by the 64 lanes of wavefront 0 with the workgroup's
 // max (uniform) and the leaf count arrive_wave0 returned.  Every lane returns
 // the tensor-wide max, or NaN if this workgroup gave up waiting.
+//
+// Up to 256 workgroups, two rounds of polls are in flight: round k + 1 is
+// issued before round k is checked, so a store is seen about half a round
+// sooner (a round is a trip to the memory side, about 0.8 us under load).
+// A check only accepts values loaded after the previous check began, so the
+// protocol is unchanged.  Cold per call: [4096, 1600] at B = 64 8.64 ->
+// 8.21 us, [8192, 3584] at B = 128 19.7 -> 19.6 us, [4096, 4096] at B = 128
+// unchanged.
 __device__ float grid_max_wave0(float wg_max, unsigned long long leaf_count, char* __restrict__ ws,
                                 unsigned spin_limit) {
   const int lane = threadIdx.x & 63;
@@ -667,22 +698,33 @@ __device__ float grid_max_wave0(float wg_max, unsigned long long leaf_count, cha
     for (unsigned j = gridDim.x + lane; j < kMaxSlots; j += 64)
       store_agent(slot_of(ws, j), static_cast<unsigned long long>(epoch) << 32);
   unsigned m = 0, spins = 0;
-  while (true) {
-    bool ok = true;
-    unsigned mm = 0;
-    for (unsigned j = lane; j < gridDim.x; j += 64) {
-      const unsigned long long v = load_agent(slot_of(ws, j));
-      ok = ok && static_cast<unsigned>(v >> 32) == epoch;
-      mm = max(mm, static_cast<unsigned>(v));
+  bool ready = false;
+  if (gridDim.x <= 4 * 64) {
+    unsigned long long ra[4], rb[4];
+    poll_round(ws, lane, ra);
+    while (true) {
+      poll_round(ws, lane, rb);
+      if ((ready = round_ready(ra, epoch, m)) || ++spins >= spin_limit) break;
+      poll_round(ws, lane, ra);
+      if ((ready = round_ready(rb, epoch, m)) || ++spins >= spin_limit) break;
     }
-    m = mm;
-    if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
-    if (++spins >= spin_limit) {
-      if (lane == 0) store_agent(&reinterpret_cast<RootLine*>(ws)->timed_out, 1u);
-      m = 0x7FC00000u;   // quiet NaN: the codes of this workgroup become NaN
-      break;
+  } else {
+    while (true) {
+      bool ok = true;
+      unsigned mm = 0;
+      for (unsigned j = lane; j < gridDim.x; j += 64) {
+        const unsigned long long r = load_agent(slot_of(ws, j));
+        ok = ok && static_cast<unsigned>(r >> 32) == epoch;
+        mm = max(mm, static_cast<unsigned>(r));
+      }
+      m = mm;
+      if ((ready = __builtin_amdgcn_ballot_w64(!ok) == 0) || ++spins >= spin_limit) break;
+      __builtin_amdgcn_s_sleep(1);
     }
-    __builtin_amdgcn_s_sleep(1);
+  }
+  if (!ready) {
+    if (lane == 0) store_agent(&reinterpret_cast<RootLine*>(ws)->timed_out, 1u);
+    m = 0x7FC00000u;   // quiet NaN: the codes of this workgroup become NaN
   }
 #pragma unroll
   for (int k = 32; k > 0; k >>= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), k)));
@@ -1186,15 +1228,22 @@ __device__ __forceinline__ T pick(const T (&arr)[TACO_MAX_PARTS], int i) {
   return r;
 }
 
-// acc += decode(codes) * w, chunk by chunk.
-template <int NA>
+// The first part's product, as 0 + d * w would give it: one fused
+// multiply-add with +0, so that an exact product -0 becomes +0 as it does
+// when added to +0.  (The two differ only if a nonzero product rounded to
+// -0, which needs w < 2^-141, far outside the input domain.)
+__device__ __forceinline__ float first_product(float d, float w) { return fmaf(d, w, 0.0f); }
+
+// acc += decode(codes) * w, chunk by chunk (FIRST: acc = decode(codes) * w,
+// for the first part).
+template <int NA, bool FIRST = false>
 __device__ __forceinline__ void accumulate_chunks(float (&acc)[NA][8], const uint2 (&c)[NA], float w) {
 #pragma unroll
   for (int a = 0; a < NA; ++a) {
     float d[8];
     from_fp8x8(c[a], d);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[a][j] = add_product(acc[a][j], d[j], w);
+    for (int j = 0; j < 8; ++j) acc[a][j] = FIRST ? first_product(d[j], w) : add_product(acc[a][j], d[j], w);
   }
 }
 
@@ -1239,7 +1288,10 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
         wt[p] = ok ? parts.alpha[p][k] : 1.0f;
       }
 #pragma unroll
-      for (int p = 0; p < P; ++p) accumulate_chunks<NA>(acc, raw[p], 1.0f / (wt[p] * *parts.scale[p]));
+      for (int p = 0; p < P; ++p) {
+        if (p == 0) accumulate_chunks<NA, true>(acc, raw[p], 1.0f / (wt[p] * *parts.scale[p]));
+        else accumulate_chunks<NA>(acc, raw[p], 1.0f / (wt[p] * *parts.scale[p]));
+      }
     } else {
       // PC parts at a time, in a loop the compiler may not unroll (unrolled,
       // it hoists every part's loads again and the registers grow back)
@@ -1304,26 +1356,33 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     const int rv = rows_valid(tc, nblocks);
     // this lane's block in the wide layout (rows past the end read the last block)
     const int64_t kq = tc * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1);
-    float acc[NA][8];
-#pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[a][j] = 0.0f;
     // One part at a time: loading two or four parts' codes before using
     // any, or the next part's while accumulating the current one, measured
-    // 3-20% slower ([4096, 4096], B = 64, 128, 256, 2-8 parts).
+    // 3-20% slower ([4096, 4096], B = 64, 128, 256, 2-8 parts).  The part
+    // loop is written out here rather than through accumulate_chunks (the
+    // call form made the allocator spill at B = 128, TPW = 2); the first
+    // part is peeled off so that it takes one instruction per value.
+    float acc[NA][8];
     for (int p = 0; p < nparts; ++p) {
       uint2 raw[NA];
       load_codes_wide<NA>(pick(parts.q, p), kq, qd.ql, true, raw);
-      // (written out here rather than through accumulate_chunks: the call
-      // form made the allocator spill at B = 128, TPW = 2)
       const float w = 1.0f / (pick(parts.alpha, p)[kq] * *pick(parts.scale, p));
+      if (p == 0) {
 #pragma unroll
-      for (int a = 0; a < NA; ++a) {
-        float d[8];
-        from_fp8x8(raw[a], d);
+        for (int a = 0; a < NA; ++a) {
+          float d[8];
+          from_fp8x8(raw[a], d);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[a][e] = add_product(acc[a][e], d[e], w);
+          for (int e = 0; e < 8; ++e) acc[a][e] = first_product(d[e], w);
+        }
+      } else {
+#pragma unroll
+        for (int a = 0; a < NA; ++a) {
+          float d[8];
+          from_fp8x8(raw[a], d);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[a][e] = add_product(acc[a][e], d[e], w);
+        }
       }
     }
     // its vector ALUs are its bottleneck: the quad exchanges go through LDS
