@@ -1309,7 +1309,10 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
           accumulate_chunks<NA>(acc, raw[j], 1.0f / (wt[j] * *pick(parts.scale, p0 + j)));
       }
     }
-    rotate_wide<NA>(acc, qd);
+    // Quad exchanges through the LDS crossbar at B <= 128, where the vector
+    // ALUs bound this kernel: 4 parts of [4096, 4096] 20.5 -> 19.0 us,
+    // [4096, 1600] 9.2 -> 8.6 us (B = 256 measured slower that way).
+    rotate_wide<NA, (B <= 128)>(acc, qd);
     store_wide_bf16<NA, TACO_NT_SUM_STORES != 0>(out + k * C16, acc, Blk<B>::rsqrt_b * qd.debt, qd.ql, ok);
   }
 }
