@@ -560,6 +560,24 @@ def test_decompress_sum_compress_zero_sum(engine):
     assert sz == 1.0 and np.all(az == 1.0) and np.all(parity.ordinal(qz) == 0)
 
 
+def test_decompress_sum_compress_grid_beyond_256(taco):
+    """4 parts of [4096, 1600] at block 64: one tile per wavefront and two
+    workgroups per CU, 400 workgroups, so the barrier takes its polling
+    loop for grids beyond 256 (the others poll two rounds deep)."""
+    parts = [W.bf16_bits(W.make("gpt2_1p5b", seed=70 + p)) for p in range(4)]
+    ws = torch.zeros(taco.load().taco_decompress_sum_compress_workspace_bytes(4096, 1600, 64),
+                     dtype=torch.uint8, device="cuda")
+    trip = [oracle.compress(b, 64) for b in parts]
+    gparts = [(torch.from_numpy(q).cuda(), torch.from_numpy(a).cuda(),
+               torch.tensor([s], dtype=torch.float32).cuda()) for q, a, s in trip]
+    got = [t.clone() for t in taco.decompress_sum_compress(gparts, 64, workspace=ws)]
+    assert not taco.workspace_timed_out(ws)
+    two = taco.decompress_sum_compress(gparts, 64, single_pass=False)
+    for a, b in zip(got, two):
+        assert torch.equal(a, b)
+    run_decompress_sum_compress(taco, parts, 64)
+
+
 def test_full_size_decompress_sum_compress(engine):
     taco = engine
     """The decompress-sum workload (4 parts of [4096, 4096], block 256)."""
