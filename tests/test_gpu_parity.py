@@ -215,7 +215,9 @@ def test_fused_matches_two_pass_bitwise(taco):
              ("tiny", 256, 256), ("gpt3_6p7b_grad", 1024, 128), ("dsum_part", 17, 256),
              ("qwen_7b", 4096, 64), ("gpt2_1p5b", 4095, 64), ("qwen_7b", 4095, 128),
              ("gpt3_6p7b_act", 4096, 128), ("qwen_7b", 8192, 128), ("qwen_7b", 5120, 128),
-             ("qwen_7b", 6144, 64), ("qwen_7b", 8192, 256)]
+             ("qwen_7b", 6144, 64), ("qwen_7b", 8192, 256),
+             # B = 256 holding y through LDS with a ragged last tile (one tile, and 3,584)
+             ("tiny", 3, 256), ("qwen_7b", 4095, 256)]
     for name, tokens, block in cases:
         print(f"[case] fused vs two-pass {name} tokens={tokens} block={block}", flush=True)
         x = W.make(name, seed=tokens, tokens=tokens).cuda()
