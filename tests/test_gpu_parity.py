@@ -373,6 +373,35 @@ def test_barrier_counts_cross_bit_31_and_bit_32(taco, calls):
         assert not taco.workspace_timed_out(ws2)
 
 
+def test_barrier_over_many_calls_on_one_workspace(taco):
+    """2000 single-pass calls on one workspace, cycling through grids of 16,
+    200, 256 and 224 workgroups (y held at B = 64 and 128, x held at
+    B = 128): every result bitwise equal to the same call on a fresh
+    workspace, and no poll ever gives up."""
+    cases = [("tiny", 256, 64), ("gpt2_1p5b", 4096, 64), ("gpt3_6p7b_act", 4096, 128), ("qwen_7b", 8192, 128)]
+    xs, refs = [], []
+    for name, tokens, block in cases:
+        x = W.make(name, seed=90, tokens=tokens).cuda()
+        assert taco.is_single_pass(*x.shape, block)
+        fresh = torch.zeros(taco.workspace_bytes(*x.shape, block), dtype=torch.uint8, device="cuda")
+        xs.append((x, block))
+        refs.append(_compress_with(taco, x, block, True, fresh))
+    ws = torch.zeros(taco.workspace_bytes(8192, 3584, 128), dtype=torch.uint8, device="cuda")
+    print("[case] 2000 fused compress calls on one workspace", flush=True)
+    outs = [[torch.empty_like(t) for t in r] for r in refs]
+    for it in range(500):
+        for k, (x, block) in enumerate(xs):
+            q, a, s = outs[k]
+            taco.compress(x, block, q=q, alpha=a, scale=s, workspace=ws)
+            if it % 50 == 49 or it == 0:
+                for r, t in zip(refs[k], outs[k]):
+                    assert torch.equal(r, t), (it, cases[k])
+    for k in range(len(xs)):
+        for r, t in zip(refs[k], outs[k]):
+            assert torch.equal(r, t)
+    assert not taco.workspace_timed_out(ws)
+
+
 def test_determinism(engine):
     taco = engine
     x = W.make("gpt2_1p5b", seed=3, tokens=512).cuda()
