@@ -439,6 +439,107 @@ __device__ __forceinline__ void codes_to_lds_mfma(const f32x4_t y, float c, int 
   *reinterpret_cast<int*>(lds + n * Blk<B>::kCodeRowMfma + 16 * mt + 4 * g) = wd;
 }
 
+// ============================================================== LDS staging of x
+//
+// The compress kernels stage x through LDS: each wavefront copies its tiles
+// into its own LDS region with global_load_lds_dwordx4 (16 bytes per lane
+// written straight to LDS at lane-linear positions, 1 KiB per instruction),
+// so every load instruction covers whole cache lines instead of the 64-byte
+// pieces of loads in the MFMA operand layout; the B operand is then read
+// from LDS.  Which global chunk a lane fetches is free as long as each
+// instruction covers its 1 KiB, so chunk k of block n is fetched by the lane
+// that writes position k ^ swz(n) of the block's LDS row: the 16 columns of
+// one K-step then read 16 different 16-byte bank groups.
+template <int B>
+struct LdsTile {
+  static constexpr int C16 = B / 8;                        // 16-byte chunks per block
+  static constexpr int kBytes = kTileBlocks * B * 2;       // one bf16 tile
+  static constexpr int kCopies = kBytes / 1024;            // copy instructions per tile
+  // B = 64: a 256-byte LDS row holds two blocks, so the low bit of n picks
+  // the half and the swizzle uses the next three; otherwise the low four.
+  static __device__ __forceinline__ int swz(int n) { return B == 64 ? (n >> 1) & 7 : n & 15; }
+};
+
+// One gfx950 direct-to-LDS copy: lane i writes the 16 bytes at base + off
+// (base wave-uniform, in an SGPR pair; off a per-lane byte offset) to LDS
+// address lds + 16 i (lds is wave-uniform, in m0), non-temporal like the
+// direct loads.  Written as inline asm because with the compiler's builtin it
+// waits for every copy in flight before the wavefront's first LDS read
+// (vmcnt(0)), which serialises each tile's rotation behind all of the
+// wavefront's copies; the caller waits instead with wait_copies, tile by
+// tile.  One wait state separates the write of m0 from the copy that reads
+// it.  No VGPR is written, and the offset VGPR is read at issue.  Nothing
+// else in these kernels uses m0.
+// (clang warns that m0 is a reserved register and its clobber may not be
+// honoured; the compiler uses m0 nowhere in this file on gfx950, which
+// tests/test_build_checks.py checks on the generated assembly.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void copy16_to_lds(const uint4* base, unsigned off, unsigned lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+#endif
+}
+#pragma clang diagnostic pop
+
+// Waits until at most N vector memory operations of the wavefront are in
+// flight.  Loads complete in issue order, so after the copies of tiles
+// 0..i and then of N / kCopies more tiles, wait_copies<N> means tiles 0..i
+// have landed (earlier operations, such as the barrier's leaf add and load,
+// only make it wait longer).  The memory clobber keeps the LDS reads after it;
+// the scheduling barrier keeps the previous tile's matrix and vector work
+// before it (the scheduler would otherwise sink some of it below the wait).
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
+// Copies tile t (clamped by the caller) into lds_tile; blocks past the end of
+// the tensor are filled with the tile's last block, as load_tile_mfma does.
+template <int B>
+__device__ __forceinline__ void copy_tile_to_lds(const uint4* __restrict__ x, int64_t t, int64_t nblocks,
+                                                 char* lds_tile) {
+  constexpr int C16 = LdsTile<B>::C16;
+  const int lane = threadIdx.x & 63;
+  const int rv = rows_valid(t, nblocks);
+  // t is wave-uniform, so the tile's address goes to SGPRs and each copy
+  // needs one offset VGPR (the same for every whole tile)
+  const uint4* tile = reinterpret_cast<const uint4*>(uniform_u64(reinterpret_cast<uint64_t>(x + t * (kTileBlocks * C16))));
+  const unsigned base = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_tile)));
+#pragma unroll
+  for (int d = 0; d < LdsTile<B>::kCopies; ++d) {
+    const int pos = 64 * d + lane;
+    const int n = pos / C16, p = pos % C16;
+    const int row = n < rv ? n : rv - 1;
+    copy16_to_lds(tile, 16u * static_cast<unsigned>(row * C16 + (p ^ LdsTile<B>::swz(n))), base + 1024 * d);
+  }
+}
+
+template <int B>
+__device__ __forceinline__ void read_tile_from_lds(const char* lds_tile, uint4 (&xr)[B / 32]) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int kt = 0; kt < B / 32; ++kt)
+    xr[kt] = *reinterpret_cast<const uint4*>(
+        lds_tile + 16 * (n * LdsTile<B>::C16 + ((4 * kt + g) ^ LdsTile<B>::swz(n))));
+}
+
+// Waits until this wavefront's LDS reads have returned (before a copy may
+// overwrite the region they read).
+__device__ __forceinline__ void lds_reads_done() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
 // Two-pass compression, for tensors whose rotated blocks do not fit in the
 // resident wavefronts' registers (or when the single pass is switched off):
 // a statistics kernel (alpha and per-workgroup max) and a quantisation kernel
@@ -808,99 +909,12 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_kernel(
   }
 }
 
-// The same kernel with x staged through LDS, for the configurations that
-// hold y (a workgroup's tiles then take at most 128 KiB, within gfx950's
-// 160 KiB of LDS per CU; at B = 256 one tile per wavefront, 126 VGPRs, and
-// [4096, 4096] 14.4 -> 13.9 us against the direct loads).  Each wavefront copies its tiles into its own LDS
-// region with global_load_lds_dwordx4 (16 bytes per lane written straight to
-// LDS at lane-linear positions, 1 KiB per instruction), so every load
-// instruction covers whole cache lines instead of the 64-byte pieces of the
-// direct MFMA-layout loads; the B operand then comes from LDS.  Which global
-// chunk a lane fetches is free as long as each instruction covers its 1 KiB,
-// so chunk k of block n is fetched by the lane that writes position
-// k ^ swz(n) of the block's LDS row: the 16 columns of one K-step then read
-// 16 different 16-byte bank groups.  The arithmetic per tile, and so the
-// result, is that of compress_fused_kernel.
-template <int B>
-struct LdsTile {
-  static constexpr int C16 = B / 8;                        // 16-byte chunks per block
-  static constexpr int kBytes = kTileBlocks * B * 2;       // one bf16 tile
-  static constexpr int kCopies = kBytes / 1024;            // copy instructions per tile
-  // B = 64: a 256-byte LDS row holds two blocks, so the low bit of n picks
-  // the half and the swizzle uses the next three; otherwise the low four.
-  static __device__ __forceinline__ int swz(int n) { return B == 64 ? (n >> 1) & 7 : n & 15; }
-};
-
-// One gfx950 direct-to-LDS copy: lane i writes the 16 bytes at base + off
-// (base wave-uniform, in an SGPR pair; off a per-lane byte offset) to LDS
-// address lds + 16 i (lds is wave-uniform, in m0), non-temporal like the
-// direct loads.  Written as inline asm because with the compiler's builtin it
-// waits for every copy in flight before the wavefront's first LDS read
-// (vmcnt(0)), which serialises each tile's rotation behind all of the
-// wavefront's copies; the caller waits instead with wait_copies, tile by
-// tile.  One wait state separates the write of m0 from the copy that reads
-// it.  No VGPR is written, and the offset VGPR is read at issue.  Nothing
-// else in these kernels uses m0.
-// (clang warns that m0 is a reserved register and its clobber may not be
-// honoured; the compiler uses m0 nowhere in this file on gfx950, which
-// tests/test_build_checks.py checks on the generated assembly.)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void copy16_to_lds(const uint4* base, unsigned off, unsigned lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-               :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
-#endif
-}
-#pragma clang diagnostic pop
-
-// Waits until at most N vector memory operations of the wavefront are in
-// flight.  Loads complete in issue order, so after the copies of tiles
-// 0..i and then of N / kCopies more tiles, wait_copies<N> means tiles 0..i
-// have landed (earlier operations, such as the barrier's leaf add and load,
-// only make it wait longer).  The memory clobber keeps the LDS reads after it;
-// the scheduling barrier keeps the previous tile's matrix and vector work
-// before it (the scheduler would otherwise sink some of it below the wait).
-template <int N>
-__device__ __forceinline__ void wait_copies() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-  __builtin_amdgcn_sched_barrier(0);
-#endif
-}
-
-// Copies tile t (clamped by the caller) into lds_tile; blocks past the end of
-// the tensor are filled with the tile's last block, as load_tile_mfma does.
-template <int B>
-__device__ __forceinline__ void copy_tile_to_lds(const uint4* __restrict__ x, int64_t t, int64_t nblocks,
-                                                 char* lds_tile) {
-  constexpr int C16 = LdsTile<B>::C16;
-  const int lane = threadIdx.x & 63;
-  const int rv = rows_valid(t, nblocks);
-  // t is wave-uniform, so the tile's address goes to SGPRs and each copy
-  // needs one offset VGPR (the same for every whole tile)
-  const uint4* tile = reinterpret_cast<const uint4*>(uniform_u64(reinterpret_cast<uint64_t>(x + t * (kTileBlocks * C16))));
-  const unsigned base = __builtin_amdgcn_readfirstlane(
-      static_cast<unsigned>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds_tile)));
-#pragma unroll
-  for (int d = 0; d < LdsTile<B>::kCopies; ++d) {
-    const int pos = 64 * d + lane;
-    const int n = pos / C16, p = pos % C16;
-    const int row = n < rv ? n : rv - 1;
-    copy16_to_lds(tile, 16u * static_cast<unsigned>(row * C16 + (p ^ LdsTile<B>::swz(n))), base + 1024 * d);
-  }
-}
-
-template <int B>
-__device__ __forceinline__ void read_tile_from_lds(const char* lds_tile, uint4 (&xr)[B / 32]) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-#pragma unroll
-  for (int kt = 0; kt < B / 32; ++kt)
-    xr[kt] = *reinterpret_cast<const uint4*>(
-        lds_tile + 16 * (n * LdsTile<B>::C16 + ((4 * kt + g) ^ LdsTile<B>::swz(n))));
-}
-
+// The same kernel with x staged through LDS (see "LDS staging of x" above),
+// for the configurations that hold y: a workgroup's tiles then take at most
+// 128 KiB, within gfx950's 160 KiB of LDS per CU (at B = 256 one tile per
+// wavefront, 126 VGPRs; [4096, 4096] 14.4 -> 13.9 us against the direct
+// loads).  The arithmetic per tile, and so the result, is that of
+// compress_fused_kernel.
 template <int B, int TPW, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void compress_fused_lds_kernel(
     const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
@@ -996,14 +1010,6 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_lds_kernel(
 // wavefront, cold: 23.2 us with the direct loads (21.4 us of it remained
 // with the barrier taken out, so the loads themselves were the cost), 19.8 us
 // with the ring.
-__device__ __forceinline__ void lds_reads_done() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-#endif
-}
-
 template <int B, int TPW, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void compress_fused_ring_kernel(
     const uint4* __restrict__ x, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
@@ -1504,7 +1510,9 @@ __global__ __launch_bounds__(64 * WAVES) void compress_streaming_kernel(
     uint4* __restrict__ q) {
   constexpr int NK = B / 32, NM = B / 16, SROW = Blk<B>::kCodeRowMfma;
   __shared__ float red[WAVES];
-  __shared__ __attribute__((aligned(16))) char lds_all[WAVES][kTileBlocks * SROW];
+  constexpr int TB = LdsTile<B>::kBytes;
+  static_assert(kTileBlocks * SROW <= TB, "codes staged in the x tile");
+  __shared__ __attribute__((aligned(1024))) char lds_all[WAVES][TB];
   char* lds = lds_all[threadIdx.x >> 6];
   const HadFrag F = make_hadamard_fragments();
   const int lane = threadIdx.x & 63, n = lane & 15;
@@ -1514,7 +1522,15 @@ __global__ __launch_bounds__(64 * WAVES) void compress_streaming_kernel(
   const int rv = rows_valid(tc, nblocks);
   const int row = n < rv ? n : rv - 1;
   uint4 xr[NK];
-  load_tile_mfma<B, true>(x, tc, nblocks, xr);
+  // x through LDS (1 KiB of whole cache lines per copy instruction, as in
+  // the fused kernels), then into the MFMA operand registers; the tile's
+  // region stages the codes afterwards.  [4096, 4096] at B = 128, cold:
+  // per-block guard 11.8 -> 10.7 us, delayed scale 13.7 -> 11.9 us
+  // ([8192, 3584]: 19.2 -> 16.8 and 21.1 -> 20.2 us) against loading x
+  // straight into the operand layout.
+  copy_tile_to_lds<B>(x, tc, nblocks, lds);
+  wait_copies<0>();
+  read_tile_from_lds<B>(lds, xr);
   float s = 1.0f;
   if constexpr (MODE == kDsDelayed) {
     static_assert(kAmaxSlots == 64, "one amax slot per lane");
