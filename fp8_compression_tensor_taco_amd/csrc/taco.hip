@@ -56,6 +56,7 @@
 #include <cstddef>
 #include <initializer_list>
 #include <mutex>
+#include <utility>
 
 #include "taco.h"
 
@@ -732,13 +733,14 @@ __device__ __forceinline__ T add_agent(T* p, T v) {
 
 // Counts this workgroup into its leaf; called by the 64 lanes of wavefront 0
 // (lane 0 adds this workgroup's arrivals; in workgroup 0, lane l >= the grid's
-// leaf count advances leaf l).  The adds return nothing; then every lane loads
-// its workgroup's leaf count, with no branch around the load, so that nothing
-// waits for it before the barrier needs it.  That count lies in
-// [16 c + 1, 16 c + 16] for call number c: this workgroup's own add precedes
-// the load in the lane's program order on the same word, every leaf stood at
-// 16 c when the call began, and the call adds exactly 16.
-__device__ __forceinline__ unsigned long long arrive_wave0(char* __restrict__ ws) {
+// leaf count advances leaf l).  The adds return nothing; later every lane of
+// wavefront 0 loads its workgroup's leaf count (leaf_count), with no branch
+// around the load, so that nothing waits for it before the barrier needs it.
+// That count lies in [16 c + 1, 16 c + 16] for call number c: this
+// workgroup's own add precedes the load in wavefront 0's program order on the
+// same word, every leaf stood at 16 c when the call began, and the call adds
+// exactly 16.
+__device__ __forceinline__ void arrive_add_wave0(char* __restrict__ ws) {
   const int lane = threadIdx.x & 63;
   const unsigned l = blockIdx.x / kLeafWgs;
   const unsigned nleaves = (gridDim.x + kLeafWgs - 1) / kLeafWgs;
@@ -750,9 +752,19 @@ __device__ __forceinline__ unsigned long long arrive_wave0(char* __restrict__ ws
   } else if (blockIdx.x == 0 && static_cast<unsigned>(lane) >= nleaves) {
     add_agent(&leaf_line(ws, lane)->count, static_cast<unsigned long long>(kLeafWgs));
   }
-  return load_agent(&leaf_line(ws, l)->count);
 }
-static_assert(kLeaves == 64, "arrive_wave0 advances one unused leaf per lane");
+static_assert(kLeaves == 64, "arrive_add_wave0 advances one unused leaf per lane");
+
+// This workgroup's leaf count (other wavefronts may load it too, but only
+// wavefront 0's load is ordered after the workgroup's own add).
+__device__ __forceinline__ unsigned long long leaf_count(char* __restrict__ ws) {
+  return load_agent(&leaf_line(ws, blockIdx.x / kLeafWgs)->count);
+}
+
+__device__ __forceinline__ unsigned long long arrive_wave0(char* __restrict__ ws) {
+  arrive_add_wave0(ws);
+  return leaf_count(ws);
+}
 
 // One round of polls for grids of at most 256 workgroups: this lane's 4
 // slots (slot 0, which this call writes too, stands in past the grid).
@@ -1250,6 +1262,24 @@ __device__ __forceinline__ T pick(const T (&arr)[TACO_MAX_PARTS], int i) {
 // -0, which needs w < 2^-141, far outside the input domain.)
 __device__ __forceinline__ float first_product(float d, float w) { return fmaf(d, w, 0.0f); }
 
+// An empty asm statement that takes the 8 values and gives them back: the
+// compiler must have computed them where it stands (it emits no instruction).
+__device__ __forceinline__ void pin_values(float (&v)[8]) {
+  asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
+}
+
+// f(std::integral_constant<int, I>) for I = 0 .. N-1, expanded at compile
+// time (a loop under #pragma unroll is left rolled past the unroller's size
+// threshold, and its register arrays then go to scratch).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // acc += decode(codes) * w, chunk by chunk (FIRST: acc = decode(codes) * w,
 // for the first part).
 template <int NA, bool FIRST = false>
@@ -1343,67 +1373,60 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
 // layout), re-lays the bf16 tile out through LDS into the MFMA operand
 // layout, and continues as compress_fused_kernel (alpha, rotation on the
 // matrix cores, grid-wide max, codes).  The bf16 sum never reaches HBM, and
-// the result is bitwise equal to decompress_sum followed by compress.  The
-// part count is a runtime loop.
-template <int B, int TPW, int WAVES>
+// the result is bitwise equal to decompress_sum followed by compress.
+//
+// A tile's NP parts form a software pipeline: part p + 1's codes and alpha
+// are loaded before part p is decoded and weighed, so every wavefront keeps
+// one part's loads in flight while its vector ALUs work on another.  What
+// keeps the compiler from undoing it:
+// * the (tile, part) steps are expanded at compile time (static_for), so
+//   every index is a constant;
+// * the parts' scales are read once, up front (read at each part, through
+//   pointers it cannot prove unwritten, they were vector loads, and their
+//   wait covered the prefetched part too);
+// * each part's sums pass through pin_values, so that its adds are issued
+//   before the next part's loads are waited for (left free, the compiler
+//   deferred them into the next part and kept 32 products live: spills);
+// * scheduling barriers on both sides of each part's accumulation.
+// Cold, 4 parts, bitwise unchanged: [4096, 4096] B = 128 24.7-25.2 ->
+// 23.5-23.7 us, [4096, 1600] B = 64 16.2 -> 14.1 us, [256, 1024] B = 64
+// 8.1 -> 7.6 us.  Two to four parts ahead measured no better at B = 128, and
+// carrying the prefetch across tiles (the next tile's first part loading
+// while this tile is rotated) slower (24.2-24.5 us).
+template <int B, int TPW, int WAVES, int NP>
 __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
-    Parts parts, int nparts, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
+    Parts parts, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
     float* __restrict__ scale, char* __restrict__ ws, uint4* __restrict__ q, unsigned spin_limit) {
+  static_assert(NP >= 1 && NP <= TACO_MAX_PARTS, "part count");
   constexpr int NA = Blk<B>::NA, NK = B / 32, NM = B / 16;
   constexpr int XROW = 2 * B + 16, SROW = Blk<B>::kCodeRowMfma;
   constexpr int kLdsWave = kTileBlocks * (XROW > SROW ? XROW : SROW);
   __shared__ float red[WAVES];
   __shared__ float amax_sh;
   __shared__ __attribute__((aligned(16))) char lds_all[WAVES][kLdsWave];
-  char* lds = lds_all[threadIdx.x >> 6];
+  char* lds = lds_all[wave_in_group()];   // a scalar register, not a VGPR held to the stores
   const Quad qd;
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t wid = static_cast<int64_t>(blockIdx.x) * WAVES + wave_in_group();
   const int64_t nw = static_cast<int64_t>(gridDim.x) * WAVES;
-  // counted into the barrier first: its add returns nothing and its load is
-  // not waited for before the barrier
+  // Counted into the barrier first (the adds return nothing); the count is
+  // loaded with the last tile, while its rotations run, so that it occupies
+  // no register during the accumulation.
+  if (threadIdx.x < 64) arrive_add_wave0(ws);
   unsigned long long leaf = 0;
-  if (threadIdx.x < 64) leaf = arrive_wave0(ws);
-  f32x4_t y[TPW][NM];
-  float al[TPW];
-  float amax = 0.0f;
+  float part_scale[NP];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) {
+  for (int p = 0; p < NP; ++p)
+    part_scale[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*parts.scale[p])));
+  f32x4_t y[TPW][NM];
+  float al_r[TPW];
+  float amax = 0.0f;
+  auto finish_tile = [&](const int i, float (&acc)[NA][8]) __attribute__((always_inline)) {
     const int64_t t = wid + i * nw;
     const int64_t tc = t < ntiles ? t : ntiles - 1;
     const int rv = rows_valid(tc, nblocks);
-    // this lane's block in the wide layout (rows past the end read the last block)
-    const int64_t kq = tc * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1);
-    // One part at a time: loading two or four parts' codes before using
-    // any, or the next part's while accumulating the current one, measured
-    // 3-20% slower ([4096, 4096], B = 64, 128, 256, 2-8 parts).  The part
-    // loop is written out here rather than through accumulate_chunks (the
-    // call form made the allocator spill at B = 128, TPW = 2); the first
-    // part is peeled off so that it takes one instruction per value.
-    float acc[NA][8];
-    for (int p = 0; p < nparts; ++p) {
-      uint2 raw[NA];
-      load_codes_wide<NA>(pick(parts.q, p), kq, qd.ql, true, raw);
-      const float w = 1.0f / (pick(parts.alpha, p)[kq] * *pick(parts.scale, p));
-      if (p == 0) {
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-          float d[8];
-          from_fp8x8(raw[a], d);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[a][e] = first_product(d[e], w);
-        }
-      } else {
-#pragma unroll
-        for (int a = 0; a < NA; ++a) {
-          float d[8];
-          from_fp8x8(raw[a], d);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[a][e] = add_product(acc[a][e], d[e], w);
-        }
-      }
-    }
+    if (i == TPW - 1) leaf = leaf_count(ws);
     // its vector ALUs are its bottleneck: the quad exchanges go through LDS
     rotate_wide<NA, true>(acc, qd);
     const float r = Blk<B>::rsqrt_b * qd.debt;
@@ -1438,16 +1461,54 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     float ss = ssq[0];
 #pragma unroll
     for (int c = 1; c < kChains; ++c) ss += ssq[c];
-    al[i] = ash_scale(column_sum_rows(ss), sqrt_eb);
-    alpha[tc * kTileBlocks + (n < rv ? n : rv - 1)] = al[i];
+    const float al = ash_scale(column_sum_rows(ss), sqrt_eb);
+    al_r[i] = al;
+    alpha[tc * kTileBlocks + (n < rv ? n : rv - 1)] = al;
     float m = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) {
       m = fmaxf(fmaxf(m, fabsf(y[i][mt][0])), fabsf(y[i][mt][1]));
       m = fmaxf(fmaxf(m, fabsf(y[i][mt][2])), fabsf(y[i][mt][3]));
     }
-    if (t < ntiles && n < rv) amax = fmaxf(amax, m * (al[i] * Blk<B>::rsqrt_b));
-  }
+    if (t < ntiles && n < rv) amax = fmaxf(amax, m * (al * Blk<B>::rsqrt_b));
+  };
+  auto block_of = [&](const int i) __attribute__((always_inline)) -> int64_t {
+    const int64_t t = wid + i * nw;
+    const int64_t tc = t < ntiles ? t : ntiles - 1;
+    const int rv = rows_valid(tc, nblocks);
+    return tc * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1);
+  };
+  constexpr int NI = TPW * NP;
+  uint2 raw[2][NA];
+  float ra[2];
+  auto fetch = [&](const int it) __attribute__((always_inline)) {
+    const int i = it / NP, p = it % NP;
+    const int64_t kq = block_of(i);
+    load_codes_wide<NA>(parts.q[p], kq, qd.ql, true, raw[it & 1]);
+    ra[it & 1] = parts.alpha[p][kq];
+  };
+  fetch(0);
+  float acc[NA][8];
+  static_for<NI>([&](auto item) __attribute__((always_inline)) {
+    constexpr int it = decltype(item)::value, i = it / NP, p = it % NP;
+    if constexpr (p + 1 < NP) fetch(it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const float w = 1.0f / (ra[it & 1] * part_scale[p]);
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      float d[8];
+      from_fp8x8(raw[it & 1][a], d);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[a][e] = p == 0 ? first_product(d[e], w) : add_product(acc[a][e], d[e], w);
+    }
+#pragma unroll
+    for (int a = 0; a < NA; ++a) pin_values(acc[a]);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (p == NP - 1) {
+      finish_tile(i, acc);
+      if constexpr (it + 1 < NI) fetch(it + 1);
+    }
+  });
   const float wg = workgroup_max<WAVES>(amax, red);
   if (threadIdx.x < 64) {
     const float A = grid_max_wave0(wg, leaf, ws, spin_limit);
@@ -1461,7 +1522,7 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
   for (int i = 0; i < TPW; ++i) {
     const int64_t t = wid + i * nw;
     if (t >= ntiles) continue;
-    const float c = (al[i] * s) * Blk<B>::rsqrt_b;
+    const float c = (al_r[i] * s) * Blk<B>::rsqrt_b;
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt) codes_to_lds_mfma<B>(y[i][mt], c, mt, lds);
     __builtin_amdgcn_wave_barrier();
@@ -2021,18 +2082,35 @@ void launch_decompress_sum(const Parts& parts, int nparts, int64_t nblocks, void
 // 256-byte aligned.
 constexpr size_t kCompressWorkspace = (kSlotOffset + static_cast<size_t>(kSlotStride) * kMaxSlots + 255) / 256 * 256;
 
+// One workgroup per CU at most (as the compress): at B = 64 one tile per
+// wavefront on two workgroups per CU measured slower than two tiles per
+// wavefront on one ([4096, 1600], 4 parts: 15.8 against 13.5 us).
+template <int B, int TPW, int WAVES, int NP>
+bool try_decompress_sum_compress_np(const Parts& parts, int64_t nblocks, float sqrt_eb, float* alpha,
+                                    float* scale, char* ws, uint4* q, hipStream_t stream, unsigned polls) {
+  static const int cap = fused_grid_cap(resident_grid(decompress_sum_compress_kernel<B, TPW, WAVES, NP>, 64 * WAVES));
+  const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
+  const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
+  if (g > cap) return false;
+  hipLaunchKernelGGL((decompress_sum_compress_kernel<B, TPW, WAVES, NP>), dim3(g), dim3(64 * WAVES), 0,
+                     stream, parts, nblocks, sqrt_eb, alpha, scale, ws, q, polls);
+  return true;
+}
+
 template <int B, int TPW, int WAVES>
 bool try_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblocks, float sqrt_eb,
                                  float* alpha, float* scale, char* ws, uint4* q, hipStream_t stream,
                                  unsigned polls) {
-  static const int cap = std::min(resident_grid(decompress_sum_compress_kernel<B, TPW, WAVES>, 64 * WAVES),
-                                  kMaxSlots);
-  const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
-  const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
-  if (g > cap) return false;
-  hipLaunchKernelGGL((decompress_sum_compress_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
-                     stream, parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, q, polls);
-  return true;
+  switch (nparts) {
+    case 1: return try_decompress_sum_compress_np<B, TPW, WAVES, 1>(parts, nblocks, sqrt_eb, alpha, scale, ws, q, stream, polls);
+    case 2: return try_decompress_sum_compress_np<B, TPW, WAVES, 2>(parts, nblocks, sqrt_eb, alpha, scale, ws, q, stream, polls);
+    case 3: return try_decompress_sum_compress_np<B, TPW, WAVES, 3>(parts, nblocks, sqrt_eb, alpha, scale, ws, q, stream, polls);
+    case 4: return try_decompress_sum_compress_np<B, TPW, WAVES, 4>(parts, nblocks, sqrt_eb, alpha, scale, ws, q, stream, polls);
+    case 5: return try_decompress_sum_compress_np<B, TPW, WAVES, 5>(parts, nblocks, sqrt_eb, alpha, scale, ws, q, stream, polls);
+    case 6: return try_decompress_sum_compress_np<B, TPW, WAVES, 6>(parts, nblocks, sqrt_eb, alpha, scale, ws, q, stream, polls);
+    case 7: return try_decompress_sum_compress_np<B, TPW, WAVES, 7>(parts, nblocks, sqrt_eb, alpha, scale, ws, q, stream, polls);
+    default: return try_decompress_sum_compress_np<B, TPW, WAVES, 8>(parts, nblocks, sqrt_eb, alpha, scale, ws, q, stream, polls);
+  }
 }
 
 // Fused when the reduced tensor fits on chip (fewest tiles per wavefront

@@ -4,6 +4,9 @@ the device code here; nothing runs on a GPU).
 * m0 is written only by the direct-to-LDS copies' inline assembly.  clang
   warns that it may not honour an m0 clobber, so the compiler itself must use
   m0 nowhere in the library.
+* No kernel calls a function: every helper and lambda is inlined (a lambda
+  left out of line is reached through s_swappc with its captures in
+  scratch memory).
 * The fused kernels spill no VGPRs.  They wait for their LDS copies by count
   (loads complete in issue order); scratch spills are vector memory
   operations of their own, which would only make those waits longer, but a
@@ -62,3 +65,9 @@ def test_fused_kernels_do_not_spill(device_code):
             spills[name] = int(m.group(1))
     assert len(spills) >= 10, sorted(spills)
     assert all(v == 0 for v in spills.values()), {k: v for k, v in spills.items() if v}
+
+
+def test_no_kernel_calls_a_function(device_code):
+    asm, _ = device_code
+    assert "s_swappc_b64" not in asm
+    assert "s_setpc_b64" not in asm
