@@ -1245,17 +1245,6 @@ __device__ __forceinline__ float add_product(float acc, float d, float w) {
   return acc + d * w;
 }
 
-// arr[i] for a wave-uniform runtime i, by a chain of selects: indexing the
-// kernel-argument array directly with a runtime index makes the compiler copy
-// it to scratch memory.
-template <typename T>
-__device__ __forceinline__ T pick(const T (&arr)[TACO_MAX_PARTS], int i) {
-  T r = arr[0];
-#pragma unroll
-  for (int k = 1; k < TACO_MAX_PARTS; ++k) r = i == k ? arr[k] : r;
-  return r;
-}
-
 // The first part's product, as 0 + d * w would give it: one fused
 // multiply-add with +0, so that an exact product -0 becomes +0 as it does
 // when added to +0.  (The two differ only if a nonzero product rounded to
@@ -1298,63 +1287,57 @@ __device__ __forceinline__ void accumulate_chunks(float (&acc)[NA][8], const uin
 // and the 1/sqrt(B) factor.  This is the same sum as decompressing each part
 // and adding the results, with P-1 fewer transforms per block.  Wide layout:
 // each lane loads its 16 codes of every 64-element group with one 16-byte
-// load per part, all parts' loads issued before any is used, and the bf16
-// result leaves through store_wide_bf16 (staging it through LDS as
-// decompress_kernel does measured slower here: 21.5 -> 24.3 us for 4 parts).
-// At B = 256 with 4, 6 or 8 parts the loads go two parts at a time: all at
-// once took 159-226 VGPRs (2-3 wavefronts per SIMD), two at a time 128
-// (4 wavefronts), 22.8 -> 22.1 us for 4 parts of [4096, 4096]; at B = 64
-// and 128 all parts at once measured fastest.
+// load per part, and the bf16 result leaves through store_wide_bf16 (staging
+// it through LDS as decompress_kernel does measured slower here: 21.5 ->
+// 24.3 us for 4 parts).  The parts are summed in order as their loads land,
+// with DsumDepth<B, P> parts in flight ahead of the one being summed (the
+// steps expanded at compile time and pinned, as in the decompress-sum-compress
+// below): all of them at B = 64 and 128; one at B = 256, where a part takes
+// 16 VGPRs per lane.  Before, every part was waited for before the first was
+// summed (a branch around each load made the compiler wait for all of them).
+// Cold, 4 parts: [4096, 1600] B = 64 11.4 -> 10.9 us, [4096, 4096] B = 128
+// 22.4 -> 22.1 us, B = 256 22.3 -> 22.1 us; at B = 256 all parts in flight
+// measured 23.6 us, and two or four tiles per wavefront (a grid of half or a
+// quarter) 23.5 and 26.7 us.
 template <int B, int P>
-struct DsumChunk {
-  static constexpr int value = (B == 256 && P % 2 == 0 && P > 2) ? 2 : P;
+struct DsumDepth {
+  static constexpr int value = B == 256 ? (P > 1 ? 1 : 0) : P - 1;
 };
 
 template <int B, int P>
 __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
     Parts parts, int64_t nblocks, uint4* __restrict__ out) {
-  constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16, PC = DsumChunk<B, P>::value;
+  constexpr int NA = Blk<B>::NA, C16 = Blk<B>::C16, D = DsumDepth<B, P>::value;
   const Quad qd;
+  float part_scale[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+    part_scale[p] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(*parts.scale[p])));
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + wave_in_group(); t < ntiles; t += W) {
     const int64_t k = t * kTileBlocks + qd.blk;
     const bool ok = k < nblocks;
+    // rows past the end load the last block (not stored): no branch around
+    // a load, so that each part is waited for alone
+    const int64_t kl = ok ? k : nblocks - 1;
+    uint2 raw[D + 1][NA];
+    float wt[D + 1];
+    auto fetch = [&](const int p) __attribute__((always_inline)) {
+      load_codes_wide<NA>(parts.q[p], kl, qd.ql, true, raw[p % (D + 1)]);
+      wt[p % (D + 1)] = parts.alpha[p][kl];
+    };
+    static_for<D>([&](auto pc) __attribute__((always_inline)) { fetch(decltype(pc)::value); });
     float acc[NA][8];
+    static_for<P>([&](auto pc) __attribute__((always_inline)) {
+      constexpr int p = decltype(pc)::value;
+      if constexpr (p + D < P) fetch(p + D);
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate_chunks<NA, p == 0>(acc, raw[p % (D + 1)], 1.0f / (wt[p % (D + 1)] * part_scale[p]));
 #pragma unroll
-    for (int a = 0; a < NA; ++a)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc[a][j] = 0.0f;
-    if constexpr (PC == P) {
-      uint2 raw[P][NA];
-      float wt[P];
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        load_codes_wide<NA>(parts.q[p], k, qd.ql, ok, raw[p]);
-        wt[p] = ok ? parts.alpha[p][k] : 1.0f;
-      }
-#pragma unroll
-      for (int p = 0; p < P; ++p) {
-        if (p == 0) accumulate_chunks<NA, true>(acc, raw[p], 1.0f / (wt[p] * *parts.scale[p]));
-        else accumulate_chunks<NA>(acc, raw[p], 1.0f / (wt[p] * *parts.scale[p]));
-      }
-    } else {
-      // PC parts at a time, in a loop the compiler may not unroll (unrolled,
-      // it hoists every part's loads again and the registers grow back)
-#pragma unroll 1
-      for (int p0 = 0; p0 < P; p0 += PC) {
-        uint2 raw[PC][NA];
-        float wt[PC];
-#pragma unroll
-        for (int j = 0; j < PC; ++j) {
-          load_codes_wide<NA>(pick(parts.q, p0 + j), k, qd.ql, ok, raw[j]);
-          wt[j] = ok ? pick(parts.alpha, p0 + j)[k] : 1.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < PC; ++j)
-          accumulate_chunks<NA>(acc, raw[j], 1.0f / (wt[j] * *pick(parts.scale, p0 + j)));
-      }
-    }
+      for (int a = 0; a < NA; ++a) pin_values(acc[a]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     // Quad exchanges through the LDS crossbar at B <= 128, where the vector
     // ALUs bound this kernel: 4 parts of [4096, 4096] 20.5 -> 19.0 us,
     // [4096, 1600] 9.2 -> 8.6 us (B = 256 measured slower that way).
