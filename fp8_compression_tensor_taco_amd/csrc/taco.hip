@@ -1358,24 +1358,36 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
 // matrix cores, grid-wide max, codes).  The bf16 sum never reaches HBM, and
 // the result is bitwise equal to decompress_sum followed by compress.
 //
-// A tile's NP parts form a software pipeline: part p + 1's codes and alpha
-// are loaded before part p is decoded and weighed, so every wavefront keeps
-// one part's loads in flight while its vector ALUs work on another.  What
-// keeps the compiler from undoing it:
+// A tile's NP parts form a software pipeline: the tile's later parts' codes
+// and alphas are loaded (up to dsc_depth of them ahead) while part p is
+// decoded and weighed, and part p waits for its own loads only, so every
+// wavefront keeps loads in flight while its vector ALUs work.  What keeps
+// the compiler from undoing it:
 // * the (tile, part) steps are expanded at compile time (static_for), so
 //   every index is a constant;
 // * the parts' scales are read once, up front (read at each part, through
 //   pointers it cannot prove unwritten, they were vector loads, and their
-//   wait covered the prefetched part too);
+//   wait covered the prefetched parts too);
 // * each part's sums pass through pin_values, so that its adds are issued
 //   before the next part's loads are waited for (left free, the compiler
 //   deferred them into the next part and kept 32 products live: spills);
 // * scheduling barriers on both sides of each part's accumulation.
-// Cold, 4 parts, bitwise unchanged: [4096, 4096] B = 128 24.7-25.2 ->
-// 23.5-23.7 us, [4096, 1600] B = 64 16.2 -> 14.1 us, [256, 1024] B = 64
-// 8.1 -> 7.6 us.  Two to four parts ahead measured no better at B = 128, and
-// carrying the prefetch across tiles (the next tile's first part loading
-// while this tile is rotated) slower (24.2-24.5 us).
+// Cold, 4 parts, bitwise unchanged: [4096, 4096] B = 128 24.7-25.2 -> 23.5-
+// 23.7 us with one part ahead, 22.9-23.2 us with three; [4096, 1600] B = 64
+// 16.2 -> 14.0 us; [256, 1024] B = 64 8.1 -> 7.6 us.  Carrying the prefetch
+// across tiles (the next tile's first part loading while this tile is
+// rotated) measured slower (24.2-24.5 us with one part ahead).
+
+// Parts in flight ahead of the one being summed in decompress_sum_compress_
+// kernel: the rest of the tile's, up to three, and fewer where that would
+// spill (B = 128 with two tiles per wavefront, which holds y for the first
+// tile while it sums the second).
+template <int B, int TPW, int NP>
+constexpr int dsc_depth() {
+  if (B == 128 && TPW == 2 && NP > 4) return NP > 6 ? 1 : 2;
+  return NP - 1 < 3 ? NP - 1 : 3;
+}
+
 template <int B, int TPW, int WAVES, int NP>
 __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     Parts parts, int64_t nblocks, float sqrt_eb, float* __restrict__ alpha,
@@ -1461,26 +1473,27 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     const int rv = rows_valid(tc, nblocks);
     return tc * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1);
   };
-  constexpr int NI = TPW * NP;
-  uint2 raw[2][NA];
-  float ra[2];
+  constexpr int NI = TPW * NP, D = dsc_depth<B, TPW, NP>(), NB = D + 1;
+  uint2 raw[NB][NA];
+  float ra[NB];
   auto fetch = [&](const int it) __attribute__((always_inline)) {
     const int i = it / NP, p = it % NP;
     const int64_t kq = block_of(i);
-    load_codes_wide<NA>(parts.q[p], kq, qd.ql, true, raw[it & 1]);
-    ra[it & 1] = parts.alpha[p][kq];
+    load_codes_wide<NA>(parts.q[p], kq, qd.ql, true, raw[it % NB]);
+    ra[it % NB] = parts.alpha[p][kq];
   };
-  fetch(0);
+  // a tile's first D parts, then part p + D while part p is summed
+  static_for<D>([&](auto c) __attribute__((always_inline)) { fetch(decltype(c)::value); });
   float acc[NA][8];
   static_for<NI>([&](auto item) __attribute__((always_inline)) {
     constexpr int it = decltype(item)::value, i = it / NP, p = it % NP;
-    if constexpr (p + 1 < NP) fetch(it + 1);
+    if constexpr (p + D < NP) fetch(it + D);
     __builtin_amdgcn_sched_barrier(0);
-    const float w = 1.0f / (ra[it & 1] * part_scale[p]);
+    const float w = 1.0f / (ra[it % NB] * part_scale[p]);
 #pragma unroll
     for (int a = 0; a < NA; ++a) {
       float d[8];
-      from_fp8x8(raw[it & 1][a], d);
+      from_fp8x8(raw[it % NB][a], d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[a][e] = p == 0 ? first_product(d[e], w) : add_product(acc[a][e], d[e], w);
     }
@@ -1489,7 +1502,9 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (p == NP - 1) {
       finish_tile(i, acc);
-      if constexpr (it + 1 < NI) fetch(it + 1);
+      static_for<D>([&](auto c) __attribute__((always_inline)) {
+        if constexpr (it + 1 + decltype(c)::value < NI) fetch(it + 1 + decltype(c)::value);
+      });
     }
   });
   const float wg = workgroup_max<WAVES>(amax, red);
