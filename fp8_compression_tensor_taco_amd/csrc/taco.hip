@@ -2082,7 +2082,7 @@ constexpr size_t kCompressWorkspace = (kSlotOffset + static_cast<size_t>(kSlotSt
 
 // One workgroup per CU at most (as the compress): at B = 64 one tile per
 // wavefront on two workgroups per CU measured slower than two tiles per
-// wavefront on one ([4096, 1600], 4 parts: 15.8 against 13.5 us).
+// wavefront on one ([4096, 1600], 4 parts: 15.0 against 13.9-14.2 us).
 template <int B, int TPW, int WAVES, int NP>
 bool try_decompress_sum_compress_np(const Parts& parts, int64_t nblocks, float sqrt_eb, float* alpha,
                                     float* scale, char* ws, uint4* q, hipStream_t stream, unsigned polls) {

@@ -1,0 +1,92 @@
+"""GPU coverage of every compiled variant of the part-count-templated kernels.
+
+The decompress-sum and the fused decompress-sum-compress are compiled once
+per part count (1-8), and the fused kernel also per block size and tiles per
+wavefront, which the library picks from the tensor's size.  Each variant is
+its own code (its own prefetch depth and unrolled steps), so each is run
+here:
+
+* decompress-sum at B = 64 and 128 for every part count, against the oracle
+  (B = 256 is covered the same way in test_gpu_parity.py);
+* the fused decompress-sum-compress for every (block, tiles per wavefront,
+  part count) it is compiled for, on random valid codes, bitwise against the
+  two-kernel composition (decompress-sum, then compress), with a check that
+  the fused kernel ran (it leaves the workspace's bf16 intermediate
+  untouched, which the two-kernel path writes).
+"""
+import numpy as np
+import pytest
+import torch
+
+from fp8_compression_tensor_taco_amd import workloads as W
+from test_gpu_parity import run_decompress_sum
+
+pytestmark = pytest.mark.gpu
+
+COMPRESS_WORKSPACE = 37120   # barrier state and partial maxima, before the intermediate
+WAVES = {64: 16, 128: 16, 256: 8}
+
+
+@pytest.fixture(scope="module")
+def taco():
+    assert torch.cuda.is_available(), "GPU tests need a GPU (no CPU fallback exists)"
+    import fp8_compression_tensor_taco_amd as taco
+    taco.load()
+    return taco
+
+
+@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize("nparts", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_decompress_sum_every_part_count(taco, block, nparts):
+    parts = [W.bf16_bits(W.make("gpt3_6p7b_act", seed=40 + p, tokens=5)) for p in range(nparts)]
+    run_decompress_sum(taco, parts, block)
+
+
+def shape_for(block, tpw, cus):
+    """A [tokens, hidden] whose tile count needs exactly `tpw` tiles per
+    wavefront on one workgroup of WAVES[block] wavefronts per CU."""
+    per_tile = 16 * block
+    lo = cus * WAVES[block] * (tpw // 2 if tpw > 1 else 0)
+    hi = cus * WAVES[block] * tpw
+    tiles = (lo + hi) // 2 + 3          # strictly inside, and not a multiple of the grid
+    hidden = 4096 if block < 256 else 8192
+    tokens = -(-tiles * per_tile // hidden)
+    assert lo < tokens * hidden // per_tile <= hi
+    return tokens, hidden
+
+
+def random_parts(tokens, hidden, block, nparts, seed):
+    rng = np.random.default_rng(seed)
+    parts = []
+    for _ in range(nparts):
+        q = rng.integers(0, 256, size=(tokens, hidden), dtype=np.uint8)
+        q[(q & 0x7F) == 0x7F] ^= 0x01                      # no E4M3 NaN codes
+        alpha = rng.uniform(0.25, 4.0, size=tokens * hidden // block).astype(np.float32)
+        scale = np.float32(rng.uniform(0.5, 50.0))
+        parts.append((torch.from_numpy(q).cuda(), torch.from_numpy(alpha).cuda(),
+                      torch.tensor([scale], dtype=torch.float32).cuda()))
+    return parts
+
+
+CONFIGS = [(64, 1), (64, 2), (64, 4), (128, 1), (128, 2), (256, 2)]
+
+
+@pytest.mark.parametrize("block,tpw", CONFIGS)
+@pytest.mark.parametrize("nparts", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_fused_decompress_sum_compress_every_variant(taco, block, tpw, nparts):
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tokens, hidden = shape_for(block, tpw, cus)
+    print(f"[case] fused dsc block={block} tiles/wavefront={tpw} parts={nparts} shape=({tokens},{hidden})",
+          flush=True)
+    parts = random_parts(tokens, hidden, block, nparts, seed=1000 * block + 10 * tpw + nparts)
+    lib = taco.load()
+    ws = torch.zeros(lib.taco_decompress_sum_compress_workspace_bytes(tokens, hidden, block),
+                     dtype=torch.uint8, device="cuda")
+    assert ws.numel() > COMPRESS_WORKSPACE
+    got = [t.clone() for t in taco.decompress_sum_compress(parts, block, 0.75, workspace=ws)]
+    torch.cuda.synchronize()
+    assert not taco.workspace_timed_out(ws)
+    assert int(torch.count_nonzero(ws[COMPRESS_WORKSPACE:])) == 0, "the two-kernel path ran"
+    ref = taco.decompress_sum_compress(parts, block, 0.75, single_pass=False)
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)

@@ -591,10 +591,11 @@ def test_decompress_sum_compress_zero_sum(engine):
     assert sz == 1.0 and np.all(az == 1.0) and np.all(parity.ordinal(qz) == 0)
 
 
-def test_decompress_sum_compress_grid_beyond_256(taco):
-    """4 parts of [4096, 1600] at block 64: one tile per wavefront and two
-    workgroups per CU, 400 workgroups, so the barrier takes its polling
-    loop for grids beyond 256 (the others poll two rounds deep)."""
+def test_decompress_sum_compress_two_tiles_per_wavefront_b64(taco):
+    """4 parts of [4096, 1600] at block 64: 6400 tiles, more than one tile per
+    wavefront fits on one workgroup per CU, so the fused kernel runs two
+    tiles per wavefront (200 workgroups); checked bitwise against the
+    two-kernel path and against the oracle."""
     parts = [W.bf16_bits(W.make("gpt2_1p5b", seed=70 + p)) for p in range(4)]
     ws = torch.zeros(taco.load().taco_decompress_sum_compress_workspace_bytes(4096, 1600, 64),
                      dtype=torch.uint8, device="cuda")
