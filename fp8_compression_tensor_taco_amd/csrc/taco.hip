@@ -1186,48 +1186,90 @@ constexpr int kOutStride = 2 * B + 32;
 // code load per lane and 64-element group; the bf16 tile goes through the
 // wavefront's LDS image and leaves lane-linearly, 1 KiB of whole cache lines
 // per store instruction (direct stores of 64-byte half lines from the
-// registers took 11.8 us instead of 8.9 on [4096, 4096], B = 128).  Each
-// wavefront issues the code loads of U tiles before using any (U = 4 at
-// B = 64, whose 1 KiB tiles are too small to keep the loads in flight
-// otherwise: 10.8 -> 10.2 us; 1 at B = 128 and 256, where more measured
-// slower).  SBLK: `scale` holds one post-rotation scale per block (the
-// per-block Dual-Scale variant) instead of one per tensor.
-template <int B, bool SBLK, int U>
+// registers took 11.8 us instead of 8.9 on [4096, 4096], B = 128).  The grid
+// holds at most kDecompressWgsPerCu<B> workgroups per CU and each wavefront
+// walks its tiles (w, w + W, ...) as a software pipeline: the next tile's
+// codes and scales are loaded before the current tile is rotated and stored.
+// Loads and stores are branch-free (rows past the tensor's end load the last
+// block and store duplicates of it), so that each wait is for the tile it
+// needs.  Cold, against one batch of tiles per wavefront (U tiles' loads
+// issued before any was used, U = 4 at B = 64, else 1): [4096, 1600] B = 64
+// 6.2 -> 4.6 us, [4096, 4096] B = 128 9.1-9.2 -> 8.5-8.7 us, [8192, 3584]
+// B = 128 15.3-16.0 -> 14.6 us, [4096, 4096] B = 256 9.9-10.1 -> 9.3-9.7 us.
+// SBLK: `scale` holds one post-rotation scale per block (the per-block
+// Dual-Scale variant) instead of one per tensor.
+template <int B>
+constexpr int kDecompressWgsPerCu = B == 64 ? 6 : 8;
+
+// Lane-linear store of a tile's padded LDS image (ROW bytes per row, STRIDE
+// apart) with every lane storing: rows past rows_valid store a copy of the
+// last valid row to its own place (identical bytes), so no store is
+// predicated.
+template <int ROW, int STRIDE, bool NT>
+__device__ __forceinline__ void lds_store_tile_clamped(const char* lds, uint4* __restrict__ g, int64_t tile,
+                                                       int rows_valid) {
+  constexpr int kChunksPerRow = ROW / 16, kChunks = kTileBlocks * kChunksPerRow;
+  static_assert(kChunks % 64 == 0, "whole store instructions");
+  const int lane = threadIdx.x & 63;
+  uint4* base = g + tile * kChunks;
+#pragma unroll
+  for (int i = 0; i < kChunks / 64; ++i) {
+    const int c = 64 * i + lane;
+    const int r0 = c / kChunksPerRow, col = c % kChunksPerRow;
+    const int r = r0 < rows_valid ? r0 : rows_valid - 1;
+    store16<NT>(&base[r * kChunksPerRow + col], *reinterpret_cast<const uint4*>(lds + r * STRIDE + 16 * col));
+  }
+}
+
+template <int B, bool SBLK>
 __global__ __launch_bounds__(kThreads) void decompress_kernel(
     const uint4* __restrict__ q, const float* __restrict__ alpha, const float* __restrict__ scale,
     int64_t nblocks, uint4* __restrict__ out) {
   constexpr int NA = Blk<B>::NA, XS = kOutStride<B>;
   __shared__ __attribute__((aligned(16))) char lds_all[kWaves][kTileBlocks * XS];
-  char* lds = lds_all[threadIdx.x >> 6];
+  char* lds = lds_all[wave_in_group()];
   const Quad qd;
   const float s = SBLK ? 1.0f : *scale;
   const int64_t ntiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t W = static_cast<int64_t>(gridDim.x) * kWaves;
-  for (int64_t t0 = static_cast<int64_t>(blockIdx.x) * kWaves + wave_in_group(); t0 < ntiles;
-       t0 += W * U) {
-    uint2 raw[U][NA];
-    float al[U], sk[U];
+  int64_t t = static_cast<int64_t>(blockIdx.x) * kWaves + wave_in_group();
+  if (t >= ntiles) return;
+  // Tile tt's codes, alpha and scale into (raw, al, sk); past the last tile
+  // of this wavefront it loads tile `own` again (already in L2), not a new one.
+  auto fetch = [&](int64_t tt, int64_t own, uint2 (&raw)[NA], float& al, float& sk)
+      __attribute__((always_inline)) {
+    const int64_t tc = tt < ntiles ? tt : own;
+    const int rv = rows_valid(tc, nblocks);
+    const int64_t k = tc * kTileBlocks + (qd.blk < rv ? qd.blk : rv - 1);
+    load_codes_wide<NA>(q, k, qd.ql, true, raw);
+    al = alpha[k];
+    sk = SBLK ? scale[k] : s;
+  };
+  auto process = [&](int64_t tt, const uint2 (&raw)[NA], float al, float sk) __attribute__((always_inline)) {
+    float v[NA][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t k = (t0 + u * W) * kTileBlocks + qd.blk;
-      const bool ok = t0 + u * W < ntiles && k < nblocks;
-      load_codes_wide<NA>(q, k, qd.ql, ok, raw[u]);
-      al[u] = ok ? alpha[k] : 1.0f;
-      sk[u] = SBLK ? (ok ? scale[k] : 1.0f) : s;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t t = t0 + u * W;
-      if (t >= ntiles) break;
-      float v[NA][8];
-#pragma unroll
-      for (int a = 0; a < NA; ++a) from_fp8x8(raw[u][a], v[a]);
-      rotate_wide<NA>(v, qd);
-      wide_tile_to_lds<NA, XS>(v, (Blk<B>::rsqrt_b / (al[u] * sk[u])) * qd.debt, qd, lds);
-      __builtin_amdgcn_wave_barrier();
-      lds_store_tile_to_global<2 * B, XS, TACO_NT_OUT_STORES != 0>(lds, out, t, rows_valid(t, nblocks));
-      __builtin_amdgcn_wave_barrier();
-    }
+    for (int a = 0; a < NA; ++a) from_fp8x8(raw[a], v[a]);
+    rotate_wide<NA>(v, qd);
+    wide_tile_to_lds<NA, XS>(v, (Blk<B>::rsqrt_b / (al * sk)) * qd.debt, qd, lds);
+    __builtin_amdgcn_wave_barrier();
+    lds_store_tile_clamped<2 * B, XS, TACO_NT_OUT_STORES != 0>(lds, out, tt, rows_valid(tt, nblocks));
+    __builtin_amdgcn_wave_barrier();
+  };
+  // two register sets, unrolled by two so that neither is copied
+  uint2 ra[NA], rb[NA];
+  float aa, ab, sa, sb;
+  fetch(t, t, ra, aa, sa);
+  while (true) {
+    fetch(t + W, t, rb, ab, sb);
+    __builtin_amdgcn_sched_barrier(0);   // the prefetch stays ahead of the rotation
+    process(t, ra, aa, sa);
+    t += W;
+    if (t >= ntiles) break;
+    fetch(t + W, t, ra, aa, sa);
+    __builtin_amdgcn_sched_barrier(0);
+    process(t, rb, ab, sb);
+    t += W;
+    if (t >= ntiles) break;
   }
 }
 
@@ -2049,8 +2091,9 @@ void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, f
 template <int B, bool SBLK>
 void launch_decompress(const uint8_t* q, const float* alpha, const float* scale, int64_t nblocks,
                        void* out, hipStream_t stream) {
-  constexpr int U = B == 64 ? 4 : 1;
-  hipLaunchKernelGGL((decompress_kernel<B, SBLK, U>), dim3((tile_grid(nblocks) + U - 1) / U), dim3(kThreads), 0,
+  const int cus = device_cu_count();
+  const int g = std::min<int>(tile_grid(nblocks), (cus > 0 ? cus : 256) * kDecompressWgsPerCu<B>);
+  hipLaunchKernelGGL((decompress_kernel<B, SBLK>), dim3(g), dim3(kThreads), 0,
                      stream, reinterpret_cast<const uint4*>(q), alpha, scale, nblocks, static_cast<uint4*>(out));
 }
 
