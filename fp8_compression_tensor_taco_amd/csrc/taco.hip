@@ -2091,8 +2091,13 @@ void launch_compress(const void* x, int64_t nblocks, float energy, uint8_t* q, f
 template <int B, bool SBLK>
 void launch_decompress(const uint8_t* q, const float* alpha, const float* scale, int64_t nblocks,
                        void* out, hipStream_t stream) {
+  // no more workgroups than fit at once: a partial second round of
+  // workgroups would start late (the per-block-scale variant at B = 128
+  // fits 7 per CU, not 8: 11.4 against 10.8 us before this cap)
   const int cus = device_cu_count();
-  const int g = std::min<int>(tile_grid(nblocks), (cus > 0 ? cus : 256) * kDecompressWgsPerCu<B>);
+  static const int cap = std::min(resident_grid(decompress_kernel<B, SBLK>, kThreads),
+                                  (cus > 0 ? cus : 256) * kDecompressWgsPerCu<B>);
+  const int g = std::min<int>(tile_grid(nblocks), cap);
   hipLaunchKernelGGL((decompress_kernel<B, SBLK>), dim3(g), dim3(kThreads), 0,
                      stream, reinterpret_cast<const uint4*>(q), alpha, scale, nblocks, static_cast<uint4*>(out));
 }
