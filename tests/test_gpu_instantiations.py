@@ -90,3 +90,58 @@ def test_fused_decompress_sum_compress_every_variant(taco, block, tpw, nparts):
     ref = taco.decompress_sum_compress(parts, block, 0.75, single_pass=False)
     for a, b in zip(got, ref):
         assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------ persistent decompress
+# The decompress grid holds at most a few workgroups per CU and each
+# wavefront walks its tiles in a loop unrolled by two.  These shapes give
+# every wavefront three or four tiles (both halves of the loop, and an odd
+# count for some) and end in a partial tile (9 blocks per row, an odd row
+# count), checked against the oracle on sampled rows: the first and last
+# tiles of the tensor and rows spread over it.
+DECOMPRESS_LOOP = {64: (576, 38229), 128: (1152, 51029), 256: (2304, 25779)}
+
+
+def sample_rows(T, n=96, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = set(range(0, 8)) | set(range(T - 8, T)) | set(int(r) for r in rng.integers(0, T, n))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("per_block", [False, True])
+@pytest.mark.parametrize("block", [64, 128, 256])
+def test_decompress_several_tiles_per_wavefront(taco, block, per_block):
+    import oracle
+    import parity
+    hidden, tokens = DECOMPRESS_LOOP[block]
+    nblocks = tokens * hidden // block
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = cus * {64: 6, 128: 8, 256: 4}[block] * 4   # at most this many in the grid
+    assert -(-nblocks // 16) > 2.5 * waves and nblocks % 16 != 0
+    print(f"[case] decompress block={block} per_block={per_block} shape=({tokens},{hidden})", flush=True)
+    rng = np.random.default_rng(block + per_block)
+    q = rng.integers(0, 256, size=(tokens, hidden), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] ^= 0x01
+    alpha = rng.uniform(0.25, 4.0, size=nblocks).astype(np.float32)
+    if per_block:
+        s = rng.uniform(0.5, 50.0, size=nblocks).astype(np.float32)
+        got = taco.decompress_blockscale(torch.from_numpy(q).cuda(), torch.from_numpy(alpha).cuda(),
+                                         torch.from_numpy(s).cuda(), block)
+    else:
+        s = np.float32(rng.uniform(0.5, 50.0))
+        got = taco.decompress(torch.from_numpy(q).cuda(), torch.from_numpy(alpha).cuda(),
+                              torch.tensor([s], dtype=torch.float32).cuda(), block)
+    got = W.bf16_bits(got)
+    rows = sample_rows(tokens, seed=block)
+    per_row = hidden // block
+    blk = (rows[:, None] * per_row + np.arange(per_row)[None, :]).reshape(-1)
+    qs, a_s = q[rows], alpha[blk]
+    if per_block:
+        ref = oracle.decompress_blockscale(qs, a_s, s[blk], block)
+        exact = oracle.decompress_blockscale_f64(qs, a_s, s[blk], block)
+        bound = parity.decompress_error_bound(qs, a_s, s[blk], block)
+    else:
+        ref = oracle.decompress(qs, a_s, s, block)
+        exact = oracle.decompress_f64(qs, a_s, s, block)
+        bound = parity.decompress_error_bound(qs, a_s, s, block)
+    parity.bf16_neighbours_ok(got[rows], ref, exact, bound, 1e-4)
