@@ -114,9 +114,9 @@ int64_t taco_num_scales(int64_t tokens, int64_t hidden, int32_t block);
  * Residency.  The single-pass kernel (taco_compress, and taco_compress_ex
  * without TACO_FLAG_TWO_PASS) meets all its workgroups at a grid-wide barrier,
  * so they must all be resident at once: its grid is at most what the device
- * holds resident (one workgroup per compute unit for taco_compress; two for
- * the fused taco_decompress_sum_compress at block 64), and no other kernel
- * may hold compute units while it runs.  A
+ * holds resident, and at most one workgroup per compute unit (the same for
+ * the fused taco_decompress_sum_compress), and no other kernel may hold
+ * compute units while it runs.  A
  * caller that overlaps compression with other kernels (e.g. a collective on
  * another stream) must pass TACO_FLAG_TWO_PASS, which never waits on another
  * workgroup.  If residency fails anyway, a workgroup gives up after
