@@ -1416,9 +1416,9 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
 // * scheduling barriers on both sides of each part's accumulation.
 // Cold, 4 parts, bitwise unchanged: [4096, 4096] B = 128 24.7-25.2 -> 23.5-
 // 23.7 us with one part ahead, 22.9-23.2 us with three; [4096, 1600] B = 64
-// 16.2 -> 14.0 us; [256, 1024] B = 64 8.1 -> 7.6 us.  Carrying the prefetch
-// across tiles (the next tile's first part loading while this tile is
-// rotated) measured slower (24.2-24.5 us with one part ahead).
+// 16.2 -> 14.0 us; [256, 1024] B = 64 8.1 -> 7.6 us.  The next tile's first
+// parts load while this tile is rotated: 23.8-24.3 -> 23.3-23.5 us on
+// [4096, 4096] (one box), 14.0 -> 13.9 us on [4096, 1600].
 
 // Parts in flight ahead of the one being summed in decompress_sum_compress_
 // kernel: the rest of the tile's, up to three, and fewer where that would
@@ -1524,7 +1524,8 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     load_codes_wide<NA>(parts.q[p], kq, qd.ql, true, raw[it % NB]);
     ra[it % NB] = parts.alpha[p][kq];
   };
-  // a tile's first D parts, then part p + D while part p is summed
+  // a tile's first D parts (the next tile's before this one is rotated), then
+  // part p + D while part p is summed
   static_for<D>([&](auto c) __attribute__((always_inline)) { fetch(decltype(c)::value); });
   float acc[NA][8];
   static_for<NI>([&](auto item) __attribute__((always_inline)) {
@@ -1543,10 +1544,12 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     for (int a = 0; a < NA; ++a) pin_values(acc[a]);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (p == NP - 1) {
-      finish_tile(i, acc);
+      // the next tile's first D parts load while this tile is rotated
       static_for<D>([&](auto c) __attribute__((always_inline)) {
         if constexpr (it + 1 + decltype(c)::value < NI) fetch(it + 1 + decltype(c)::value);
       });
+      __builtin_amdgcn_sched_barrier(0);
+      finish_tile(i, acc);
     }
   });
   const float wg = workgroup_max<WAVES>(amax, red);
