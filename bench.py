@@ -54,7 +54,7 @@ TOKENS, HIDDEN, BLOCK, NPARTS = 4096, 4096, 128, 4
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "compress_gpt3_6p7b_counters.json")
 OP_PASSES = 2                    # passes over the buffer sets per per-op graph
 PERCALL_CALLS = 32               # cold calls per op for the per-call statistics
-MAX_CPU_WORKERS = 16             # the host CPU share of one GPU on the measuring boxes
+MAX_CPU_WORKERS = 16             # the host CPU share of one GPU on the measuring hosts
 
 
 def parse():
@@ -281,7 +281,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: the operator needs no collectives and this build "
+        print(f"bench.py measures one GPU only: the operator needs no collectives and the library "
               f"has no multi-GPU path (asked for --gpus {args.gpus}, WORLD_SIZE={world}).",
               file=sys.stderr)
         sys.exit(2)

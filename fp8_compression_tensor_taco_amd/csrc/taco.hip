@@ -1394,7 +1394,7 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
 // all-gather leg [TACO pt-summary, 2.B.3]: compress(decompress_sum(parts)).
 // Fused when the reduced tensor's rotated blocks fit in the resident
 // wavefronts' VGPRs: each wavefront sums its tiles' parts in the Hadamard
-// domain and rounds to bf16 exactly as decompress_sum_kernel does (quad
+// domain and rounds to bf16 exactly as decompress_sum_kernel does (wide
 // layout), re-lays the bf16 tile out through LDS into the MFMA operand
 // layout, and continues as compress_fused_kernel (alpha, rotation on the
 // matrix cores, grid-wide max, codes).  The bf16 sum never reaches HBM, and
@@ -1418,7 +1418,7 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
 // 23.7 us with one part ahead, 22.9-23.2 us with three; [4096, 1600] B = 64
 // 16.2 -> 14.0 us; [256, 1024] B = 64 8.1 -> 7.6 us.  The next tile's first
 // parts load while this tile is rotated: 23.8-24.3 -> 23.3-23.5 us on
-// [4096, 4096] (one box), 14.0 -> 13.9 us on [4096, 1600].
+// [4096, 4096] (same device, back to back), 14.0 -> 13.9 us on [4096, 1600].
 
 // Parts in flight ahead of the one being summed in decompress_sum_compress_
 // kernel: the rest of the tile's, up to three, and fewer where that would
