@@ -1330,12 +1330,13 @@ __device__ __forceinline__ void accumulate_chunks(float (&acc)[NA][8], const uin
 // and adding the results, with P-1 fewer transforms per block.  Wide layout:
 // each lane loads its 16 codes of every 64-element group with one 16-byte
 // load per part, and the bf16 result leaves through store_wide_bf16 (staging
-// it through LDS as decompress_kernel does measured slower here: 21.5 ->
-// 24.3 us for 4 parts).  The parts are summed in order as their loads land,
-// with DsumDepth<B, P> parts in flight ahead of the one being summed (the
-// steps expanded at compile time and pinned, as in the decompress-sum-compress
-// below): all of them at B = 64 and 128; one at B = 256, where a part takes
-// 16 VGPRs per lane.  Before, every part was waited for before the first was
+// it through LDS as decompress_kernel does measured slower with the earlier
+// part loop, 21.5 -> 24.3 us for 4 parts, and with the one below the same at
+// B = 128 and 256, 11.0 -> 10.55 us on [4096, 1600] at B = 64).  The parts
+// are summed in order as their loads land, with DsumDepth<B, P> parts in
+// flight ahead of the one being summed (the steps expanded at compile time
+// and pinned, as in the decompress-sum-compress below): all of them at
+// B = 64 and 128; one at B = 256, where a part takes 16 VGPRs per lane.  Before, every part was waited for before the first was
 // summed (a branch around each load made the compiler wait for all of them).
 // Cold, 4 parts: [4096, 1600] B = 64 11.4 -> 10.9 us, [4096, 4096] B = 128
 // 22.4 -> 22.1 us, B = 256 22.3 -> 22.1 us; at B = 256 all parts in flight
