@@ -53,6 +53,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstddef>
 #include <initializer_list>
 #include <mutex>
@@ -1954,18 +1955,35 @@ __global__ __launch_bounds__(kThreads) void int8_dequant_kernel(
 
 // ----------------------------------------------------------------- host side
 
-int device_cu_count() {
+constexpr int kMaxDevices = 64;
+
+// A launch limit of the current device, computed once per device: CU counts
+// and residency differ between GPU models, so a value cached for the whole
+// process would be wrong for a second, different GPU.  cache[dev] is 0 until
+// computed; compute() returns a positive value, or a value <= 0 (not cached)
+// when the query fails.  Threads that race on a first call compute the same
+// value.
+template <typename F>
+int per_device(std::atomic<int> (&cache)[kMaxDevices], F compute) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return -1;
-  static int cached[64] = {0};
-  if (dev < 0 || dev >= 64) return -1;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      return -1;
-    cached[dev] = n;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return compute();
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    v = compute();
+    if (v > 0) cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
+}
+
+int device_cu_count() {
+  static std::atomic<int> cache[kMaxDevices];
+  return per_device(cache, [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return -1;
+    return n;
+  });
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -2022,19 +2040,22 @@ bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, flo
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
   if constexpr (HOLD_Y && TACO_FUSED_LDS != 0) {   // y held: x staged through LDS
-    static const int cap = fused_grid_cap(resident_grid(compress_fused_lds_kernel<B, TPW, WAVES>, 64 * WAVES));
+    static std::atomic<int> caps[kMaxDevices];
+    const int cap = per_device(caps, [] { return fused_grid_cap(resident_grid(compress_fused_lds_kernel<B, TPW, WAVES>, 64 * WAVES)); });
     if (g > cap) return false;
     if (launch)
       hipLaunchKernelGGL((compress_fused_lds_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
                          stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, polls);
   } else if constexpr (!HOLD_Y && TACO_FUSED_LDS != 0) {   // x held, staged through an LDS ring
-    static const int cap = fused_grid_cap(resident_grid(compress_fused_ring_kernel<B, TPW, WAVES>, 64 * WAVES));
+    static std::atomic<int> caps[kMaxDevices];
+    const int cap = per_device(caps, [] { return fused_grid_cap(resident_grid(compress_fused_ring_kernel<B, TPW, WAVES>, 64 * WAVES)); });
     if (g > cap) return false;
     if (launch)
       hipLaunchKernelGGL((compress_fused_ring_kernel<B, TPW, WAVES>), dim3(g), dim3(64 * WAVES), 0,
                          stream, x, nblocks, sqrt_eb, alpha, scale, ws, q, polls);
   } else {
-    static const int cap = fused_grid_cap(resident_grid(compress_fused_kernel<B, TPW, HOLD_Y, WAVES>, 64 * WAVES));
+    static std::atomic<int> caps[kMaxDevices];
+    const int cap = per_device(caps, [] { return fused_grid_cap(resident_grid(compress_fused_kernel<B, TPW, HOLD_Y, WAVES>, 64 * WAVES)); });
     if (g > cap) return false;
     if (launch)
       hipLaunchKernelGGL((compress_fused_kernel<B, TPW, HOLD_Y, WAVES>), dim3(g), dim3(64 * WAVES), 0,
@@ -2098,9 +2119,11 @@ void launch_decompress(const uint8_t* q, const float* alpha, const float* scale,
   // no more workgroups than fit at once: a partial second round of
   // workgroups would start late (the per-block-scale variant at B = 128
   // fits 7 per CU, not 8: 11.4 against 10.8 us before this cap)
-  const int cus = device_cu_count();
-  static const int cap = std::min(resident_grid(decompress_kernel<B, SBLK>, kThreads),
-                                  (cus > 0 ? cus : 256) * kDecompressWgsPerCu<B>);
+  static std::atomic<int> caps[kMaxDevices];
+  const int cap = per_device(caps, [] {
+    const int cus = device_cu_count();
+    return std::min(resident_grid(decompress_kernel<B, SBLK>, kThreads), (cus > 0 ? cus : 256) * kDecompressWgsPerCu<B>);
+  });
   const int g = std::min<int>(tile_grid(nblocks), cap);
   hipLaunchKernelGGL((decompress_kernel<B, SBLK>), dim3(g), dim3(kThreads), 0,
                      stream, reinterpret_cast<const uint4*>(q), alpha, scale, nblocks, static_cast<uint4*>(out));
@@ -2138,7 +2161,10 @@ constexpr size_t kCompressWorkspace = (kSlotOffset + static_cast<size_t>(kSlotSt
 template <int B, int TPW, int WAVES, int NP>
 bool try_decompress_sum_compress_np(const Parts& parts, int64_t nblocks, float sqrt_eb, float* alpha,
                                     float* scale, char* ws, uint4* q, hipStream_t stream, unsigned polls) {
-  static const int cap = fused_grid_cap(resident_grid(decompress_sum_compress_kernel<B, TPW, WAVES, NP>, 64 * WAVES));
+  static std::atomic<int> caps[kMaxDevices];
+  const int cap = per_device(caps, [] {
+    return fused_grid_cap(resident_grid(decompress_sum_compress_kernel<B, TPW, WAVES, NP>, 64 * WAVES));
+  });
   const int64_t tiles = (nblocks + kTileBlocks - 1) / kTileBlocks;
   const int64_t g = ((tiles + TPW - 1) / TPW + WAVES - 1) / WAVES;
   if (g > cap) return false;
@@ -2301,13 +2327,13 @@ static __device__ __align__(256) char scratch[kCompressWorkspace];
 namespace {
 
 std::mutex g_scratch_mutex;
-void* g_scratch_ptr[64] = {};
+void* g_scratch_ptr[kMaxDevices] = {};
 
 // The current device's copy of `scratch` (looked up once per device), or null
 // if the lookup fails.
 void* scratch_on_current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
   std::lock_guard<std::mutex> lock(g_scratch_mutex);
   if (g_scratch_ptr[dev] == nullptr) {
     void* p = nullptr;
