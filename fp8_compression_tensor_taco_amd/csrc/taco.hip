@@ -196,23 +196,51 @@ __device__ __forceinline__ void fwht_chunk(float (&v)[8]) {
   }
 }
 
-// One butterfly stage on an index bit held across the quad (CTRL: the DPP
-// quad permutation that pairs the lanes differing in it), with its sign debt c.
-// The same quad permutation through the LDS crossbar (ds_swizzle in quad
-// mode): no vector-ALU instruction, for kernels whose vector ALUs are the
-// bottleneck.  The values moved, and so every result, are those of dpp<CTRL>.
+// v[j] <- v[j] + dpp<CTRL>(v[j]) * c for the 8 values of a chunk, each in one
+// vector instruction: the quad permutation applied as a DPP modifier to the
+// first source of v_fmac_f32 (for fmaf(dpp<CTRL>(v), c, v) the compiler
+// emits a v_mov_b32_dpp and a v_fmac_f32, twice the vector instructions).
+// The same single rounding, so the same results.  A DPP source must not have
+// been written by a vector instruction in the two cycles before it is read,
+// and the compiler does not look inside inline assembly for that hazard:
+// an s_nop of two wait states on each side covers it.
 template <int CTRL>
-__device__ __forceinline__ float quad_swizzle(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x8000 | CTRL));
+__device__ __forceinline__ void fmac_dpp8(float (&v)[8], float c) {
+  static_assert(CTRL == kQuadXor1 || CTRL == kQuadXor2, "quad permutations only");
+#define TACO_FMAC_DPP(i, perm) "v_fmac_f32_dpp %" #i ", %" #i ", %8 quad_perm:" perm \
+                               " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define TACO_FMAC_DPP8(perm)                                                                  \
+  asm("s_nop 1\n\t" TACO_FMAC_DPP(0, perm) TACO_FMAC_DPP(1, perm) TACO_FMAC_DPP(2, perm)         \
+      TACO_FMAC_DPP(3, perm) TACO_FMAC_DPP(4, perm) TACO_FMAC_DPP(5, perm) TACO_FMAC_DPP(6, perm) \
+      TACO_FMAC_DPP(7, perm) "s_nop 1"                                                         \
+      : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]),     \
+        "+v"(v[7])                                                                            \
+      : "v"(c))
+  if constexpr (CTRL == kQuadXor1)
+    TACO_FMAC_DPP8("[1,0,3,2]");
+  else
+    TACO_FMAC_DPP8("[2,3,0,1]");
+#undef TACO_FMAC_DPP8
+#undef TACO_FMAC_DPP
 }
 
-template <int NA, int CTRL, bool SWIZZLE = false>
+// One butterfly stage on an index bit held across the quad (CTRL: the DPP
+// quad permutation that pairs the lanes differing in it), with its sign debt
+// c: v <- v + c * (the partner lane's v).  FUSED folds the exchange into the
+// multiply-add (fmac_dpp8); otherwise the compiler moves the partner's value
+// first (v_mov_b32_dpp, then v_fmac_f32).  Both round once: the results are
+// identical.
+template <int NA, int CTRL, bool FUSED = false>
 __device__ __forceinline__ void fwht_quad_stage(float (&v)[NA][8], float c) {
 #pragma unroll
-  for (int a = 0; a < NA; ++a)
+  for (int a = 0; a < NA; ++a) {
+    if constexpr (FUSED) {
+      fmac_dpp8<CTRL>(v[a], c);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      v[a][j] = fmaf(SWIZZLE ? quad_swizzle<CTRL>(v[a][j]) : dpp<CTRL>(v[a][j]), c, v[a][j]);
+      for (int j = 0; j < 8; ++j) v[a][j] = fmaf(dpp<CTRL>(v[a][j]), c, v[a][j]);
+    }
+  }
 }
 
 // One butterfly stage on the index bit that selects chunk c or c + H.
@@ -1114,15 +1142,15 @@ __global__ __launch_bounds__(64 * WAVES) void compress_fused_ring_kernel(
 // exact arithmetic; every kernel that rotates codes uses this one, so their
 // fp32 results agree bitwise (decompress-sum and the fused
 // decompress-sum-compress in particular).
-template <int NA, bool SWIZZLE = false>
+template <int NA, bool FUSED = false>
 __device__ __forceinline__ void rotate_wide(float (&v)[NA][8], const Quad& qd) {
 #pragma unroll
   for (int a = 0; a < NA; ++a) fwht_chunk<1>(v[a]);
-  fwht_quad_stage<NA, kQuadXor2, SWIZZLE>(v, qd.c2);  // bit 5
+  fwht_quad_stage<NA, kQuadXor2, FUSED>(v, qd.c2);    // bit 5
   if constexpr (NA >= 4) fwht_chunk_stage<NA, 2>(v);  // bit 6
   if constexpr (NA >= 8) fwht_chunk_stage<NA, 4>(v);  // bit 7
   fwht_chunk_stage<NA, 1>(v);                         // bit 3
-  fwht_quad_stage<NA, kQuadXor1, SWIZZLE>(v, qd.c1);  // bit 4
+  fwht_quad_stage<NA, kQuadXor1, FUSED>(v, qd.c1);    // bit 4
 }
 
 // One block's codes in the wide layout (a block is 2 NA 16-byte pieces), one
@@ -1250,6 +1278,9 @@ __global__ __launch_bounds__(kThreads) void decompress_kernel(
     float v[NA][8];
 #pragma unroll
     for (int a = 0; a < NA; ++a) from_fp8x8(raw[a], v[a]);
+    // separate DPP moves: with the exchanges folded into the multiply-adds
+    // (as in decompress-sum) [4096, 4096] at B = 128 measured 10.3 -> 10.4 us
+    // cold, 10.45 -> 10.7 us with per-block scales
     rotate_wide<NA>(v, qd);
     wide_tile_to_lds<NA, XS>(v, (Blk<B>::rsqrt_b / (al * sk)) * qd.debt, qd, lds);
     __builtin_amdgcn_wave_barrier();
@@ -1382,10 +1413,11 @@ __global__ __launch_bounds__(kThreads) void decompress_sum_kernel(
       for (int a = 0; a < NA; ++a) pin_values(acc[a]);
       __builtin_amdgcn_sched_barrier(0);
     });
-    // Quad exchanges through the LDS crossbar at B <= 128, where the vector
-    // ALUs bound this kernel: 4 parts of [4096, 4096] 20.5 -> 19.0 us,
-    // [4096, 1600] 9.2 -> 8.6 us (B = 256 measured slower that way).
-    rotate_wide<NA, (B <= 128)>(acc, qd);
+    // The quad exchanges folded into the multiply-adds: cold, 4 parts of
+    // [4096, 4096], B = 128 21.6 -> 21.3 us against exchanges through the LDS
+    // crossbar (ds_swizzle), B = 256 21.75 -> 21.45 us per layer against
+    // separate DPP moves (and 125 VGPRs instead of 144).
+    rotate_wide<NA, true>(acc, qd);
     store_wide_bf16<NA, TACO_NT_SUM_STORES != 0>(out + k * C16, acc, Blk<B>::rsqrt_b * qd.debt, qd.ql, ok);
   }
 }
@@ -1466,7 +1498,9 @@ __global__ __launch_bounds__(64 * WAVES) void decompress_sum_compress_kernel(
     const int64_t tc = t < ntiles ? t : ntiles - 1;
     const int rv = rows_valid(tc, nblocks);
     if (i == TPW - 1) leaf = leaf_count(ws);
-    // its vector ALUs are its bottleneck: the quad exchanges go through LDS
+    // quad exchanges folded into the multiply-adds: 21.8 -> 21.3 us cold
+    // (4 parts, [4096, 4096], B = 128) against exchanges through the LDS
+    // crossbar, which had been 1.1 us faster than separate DPP moves
     rotate_wide<NA, true>(acc, qd);
     const float r = Blk<B>::rsqrt_b * qd.debt;
     wide_tile_to_lds<NA, XROW>(acc, r, qd, lds);
