@@ -383,6 +383,12 @@ def main():
         taco.decompress_sum_compress(st["parts"], BLOCK, q=st["rq"], alpha=st["ra"], scale=st["rs"],
                                      workspace=ws_rs, single_pass=SP)
 
+    def op_two_shot(st, k=0):
+        # the compressed two-shot all-reduce of 4 ranks' [4096, 4096] tensors,
+        # emulated on this GPU: 4 compresses, then per row shard a fused
+        # decompress-sum-compress of the 4 ranks' rows and a decompress
+        taco.two_shot_allreduce([st["act"], st["grad"], st["act"], st["grad"]], BLOCK, single_pass=SP)
+
     def step(st):
         for k in range(2):
             op_compress(st, k)
@@ -408,6 +414,7 @@ def main():
     op_fns = {
         "compress": (op_compress, 2), "decompress": (op_decompress, 2), "decompress_sum": (op_sum, 1),
         "decompress_sum_compress": (op_sum_compress, 1),
+        "two_shot_allreduce_4ranks": (op_two_shot, 1),
         "compress_blockscale": (op_blockscale, 2), "decompress_blockscale": (op_blockscale_dec, 2),
         "compress_delayed": (op_delayed, 2),
         "compress_int8_tensor": (lambda st, k: op_int8(st, k, 0), 2),
@@ -415,6 +422,8 @@ def main():
         "compress_int8_block": (lambda st, k: op_int8(st, k, BLOCK), 2),
         "decompress_int8_block": (lambda st, k: op_int8_dec(st, k, BLOCK), 2),
     }
+    op_two_shot(sets[0])            # eager once, so that its outputs' shapes are known to the allocator
+    torch.cuda.synchronize()
     op_graphs = {op: (capture(lambda f=f, nk=nk: [f(st, k) for _ in range(P) for st in sets for k in range(nk)]),
                       nk * P * len(sets))
                  for op, (f, nk) in op_fns.items()}
@@ -523,6 +532,11 @@ def main():
         "decompress": N + 4 * nscales + 4 + 2 * N,
         "decompress_sum": NPARTS * (N + 4 * nscales + 4) + 2 * N,
         "decompress_sum_compress": NPARTS * (N + 4 * nscales + 4) + N + 4 * nscales + 4,
+        # 4 compresses of the whole tensors, then per shard of N/4 elements a
+        # decompress-sum-compress of 4 parts and a decompress
+        "two_shot_allreduce_4ranks": 4 * (3 * N + 4 * nscales + 4)
+        + 4 * (4 * (N // 4 + nscales + 4) + N // 4 + nscales + 4)
+        + 4 * (3 * (N // 4) + nscales + 4),
         "compress_blockscale": 3 * N + 8 * nscales,
         "decompress_blockscale": 3 * N + 8 * nscales,
         "compress_delayed": 3 * N + 4 * nscales + 4,
@@ -594,8 +608,10 @@ def main():
         "ops": {op: op_entry(op, True) for op in ops},
         "extra_ops": {op: op_entry(op, False) for op in extra},
         "extra_ops_note": "not part of the step: decompress_sum_compress (4 parts -> FP8 of their bf16 "
-                          "sum), the per-block-guard and delayed-scale Dual-Scale variants, and the INT8 "
-                          "degrade path (absmax per tensor: two kernels, x read twice; per 128-block)",
+                          "sum), the per-block-guard and delayed-scale Dual-Scale variants, the INT8 "
+                          "degrade path (absmax per tensor: two kernels, x read twice; per 128-block), "
+                          "and two_shot_allreduce_4ranks (the compressed two-shot all-reduce of 4 ranks' "
+                          "tensors emulated on one GPU: 12 calls, all 4 ranks' work)",
         "warm_ops": {op: {"avg_us": round(v, 3),
                           "algorithmic_GBps": round(alg[op] / (v * 1e-6) / 1e9, 1)} for op, v in warm_us.items()},
         "warm_ops_note": "Infinity-Cache resident: back-to-back calls on one buffer set; not the metric",

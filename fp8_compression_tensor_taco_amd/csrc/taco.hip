@@ -2105,10 +2105,16 @@ bool try_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, flo
 // per element) and rotate it again after the barrier, which covers 1.5 to 2
 // times as much: [8192, 4096] at B = 128 or 256, [8192, 3072] at B = 64.
 // Larger tensors take the two-pass path.  Every variant issues the same
-// MFMA sequence per tile, so all give identical results.
+// MFMA sequence per tile, so all give identical results.  With one tile per
+// wavefront, workgroups of 4 or 8 wavefronts come first, so that a small
+// tensor spreads over up to four times as many CUs (each workgroup still on
+// a CU of its own): cold, [256, 1024] at B = 64 5.24 -> 4.90 us,
+// [1024, 4096] at B = 128 7.86 -> 7.60 us.
 template <int B>
 bool launch_fused(const uint4* x, int64_t nblocks, float sqrt_eb, float* alpha, float* scale, char* ws,
                   uint4* q, hipStream_t stream, bool launch, unsigned polls) {
+  if (try_fused<B, 1, true, kWavesC / 4>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
+  if (try_fused<B, 1, true, kWavesC / 2>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
   if (try_fused<B, 1, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
   if constexpr (B <= 128)
     if (try_fused<B, 2, true, kWavesC>(x, nblocks, sqrt_eb, alpha, scale, ws, q, stream, launch, polls)) return true;
@@ -2235,9 +2241,13 @@ void launch_decompress_sum_compress(const Parts& parts, int nparts, int64_t nblo
   uint4* qv = reinterpret_cast<uint4*>(q);
   // 16 wavefronts per CU (128 VGPRs each) up to B = 128; at B = 256 the
   // rotation of the sum needs more registers, so 8 wavefronts (256 VGPRs),
-  // two tiles each.
+  // two tiles each.  As in the compress, small tensors take workgroups of 4
+  // or 8 wavefronts first, over more CUs: cold, 4 parts, [1024, 4096] at
+  // B = 128 12.2 -> 10.4 us, [256, 1024] at B = 64 7.5 -> 5.6 us.
   if (single_pass) {
     if constexpr (B <= 128) {
+      if (try_decompress_sum_compress<B, 1, kWavesC / 4>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream, polls)) return;
+      if (try_decompress_sum_compress<B, 1, kWavesC / 2>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream, polls)) return;
       if (try_decompress_sum_compress<B, 1, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream, polls)) return;
       if (try_decompress_sum_compress<B, 2, kWavesC>(parts, nparts, nblocks, sqrt_eb, alpha, scale, ws, qv, stream, polls)) return;
     } else {

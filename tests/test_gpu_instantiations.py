@@ -9,10 +9,11 @@ here:
 * decompress-sum at B = 64 and 128 for every part count, against the oracle
   (B = 256 is covered the same way in test_gpu_parity.py);
 * the fused decompress-sum-compress for every (block, tiles per wavefront,
-  part count) it is compiled for, on random valid codes, bitwise against the
-  two-kernel composition (decompress-sum, then compress), with a check that
-  the fused kernel ran (it leaves the workspace's bf16 intermediate
-  untouched, which the two-kernel path writes).
+  wavefronts per workgroup, part count) it is compiled for, on random valid
+  codes, bitwise against the two-kernel composition (decompress-sum, then
+  compress), with a check that the fused kernel ran (it leaves the
+  workspace's bf16 intermediate untouched, which the two-kernel path
+  writes).
 """
 import numpy as np
 import pytest
@@ -24,7 +25,12 @@ from test_gpu_parity import run_decompress_sum
 pytestmark = pytest.mark.gpu
 
 COMPRESS_WORKSPACE = 37120   # barrier state and partial maxima, before the intermediate
-WAVES = {64: 16, 128: 16, 256: 8}
+# The library's fused configurations (tiles per wavefront, wavefronts per
+# workgroup) in the order it tries them; it takes the first whose grid of
+# one workgroup per CU holds every tile.
+ORDER = {64: [(1, 4), (1, 8), (1, 16), (2, 16), (4, 16)],
+         128: [(1, 4), (1, 8), (1, 16), (2, 16)],
+         256: [(2, 8)]}
 
 
 @pytest.fixture(scope="module")
@@ -42,12 +48,15 @@ def test_decompress_sum_every_part_count(taco, block, nparts):
     run_decompress_sum(taco, parts, block)
 
 
-def shape_for(block, tpw, cus):
-    """A [tokens, hidden] whose tile count needs exactly `tpw` tiles per
-    wavefront on one workgroup of WAVES[block] wavefronts per CU."""
+def shape_for(block, tpw, waves, cus):
+    """A [tokens, hidden] whose tile count selects exactly the configuration
+    (tpw tiles per wavefront, `waves` wavefronts per workgroup): more tiles
+    than the previous configuration in ORDER holds, at most what this one
+    does."""
     per_tile = 16 * block
-    lo = cus * WAVES[block] * (tpw // 2 if tpw > 1 else 0)
-    hi = cus * WAVES[block] * tpw
+    k = ORDER[block].index((tpw, waves))
+    lo = cus * ORDER[block][k - 1][0] * ORDER[block][k - 1][1] if k > 0 else 0
+    hi = cus * tpw * waves
     tiles = (lo + hi) // 2 + 3          # strictly inside, and not a multiple of the grid
     hidden = 4096 if block < 256 else 8192
     tokens = -(-tiles * per_tile // hidden)
@@ -68,17 +77,17 @@ def random_parts(tokens, hidden, block, nparts, seed):
     return parts
 
 
-CONFIGS = [(64, 1), (64, 2), (64, 4), (128, 1), (128, 2), (256, 2)]
+CONFIGS = [(b, t, w) for b, order in ORDER.items() for t, w in order]
 
 
-@pytest.mark.parametrize("block,tpw", CONFIGS)
+@pytest.mark.parametrize("block,tpw,waves", CONFIGS)
 @pytest.mark.parametrize("nparts", [1, 2, 3, 4, 5, 6, 7, 8])
-def test_fused_decompress_sum_compress_every_variant(taco, block, tpw, nparts):
+def test_fused_decompress_sum_compress_every_variant(taco, block, tpw, waves, nparts):
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    tokens, hidden = shape_for(block, tpw, cus)
-    print(f"[case] fused dsc block={block} tiles/wavefront={tpw} parts={nparts} shape=({tokens},{hidden})",
-          flush=True)
-    parts = random_parts(tokens, hidden, block, nparts, seed=1000 * block + 10 * tpw + nparts)
+    tokens, hidden = shape_for(block, tpw, waves, cus)
+    print(f"[case] fused dsc block={block} tiles/wavefront={tpw} wavefronts={waves} parts={nparts} "
+          f"shape=({tokens},{hidden})", flush=True)
+    parts = random_parts(tokens, hidden, block, nparts, seed=1000 * block + 100 * waves + 10 * tpw + nparts)
     lib = taco.load()
     ws = torch.zeros(lib.taco_decompress_sum_compress_workspace_bytes(tokens, hidden, block),
                      dtype=torch.uint8, device="cuda")

@@ -217,7 +217,11 @@ def test_fused_matches_two_pass_bitwise(taco):
              ("gpt3_6p7b_act", 4096, 128), ("qwen_7b", 8192, 128), ("qwen_7b", 5120, 128),
              ("qwen_7b", 6144, 64), ("qwen_7b", 8192, 256),
              # B = 256 holding y through LDS with a ragged last tile (one tile, and 3,584)
-             ("tiny", 3, 256), ("qwen_7b", 4095, 256)]
+             ("tiny", 3, 256), ("qwen_7b", 4095, 256),
+             # one tile per wavefront on workgroups of 8, 4 and 16 wavefronts (on
+             # 256 CUs: 1,536, 200, 3,125 and 3,072 tiles)
+             ("gpt2_1p5b", 983, 64), ("dsum_part", 1536, 256), ("gpt3_6p7b_grad", 100, 128),
+             ("gpt2_1p5b", 2000, 64), ("gpt3_6p7b_act", 1536, 128)]
     for name, tokens, block in cases:
         print(f"[case] fused vs two-pass {name} tokens={tokens} block={block}", flush=True)
         x = W.make(name, seed=tokens, tokens=tokens).cuda()
