@@ -1917,7 +1917,7 @@ __global__ __launch_bounds__(kThreads) void int8_quant_tensor_kernel(
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
       const uint2 c = int8_codes_piece(v[u], s);
-      if (i < n16) store8<TACO_NT_CODE_STORES != 0>(&q[i], c);
+      store8<TACO_NT_CODE_STORES != 0>(&q[i < n16 ? i : n16 - 1], c);   // past the end: the last piece again
     }
   }
 }
@@ -1927,8 +1927,13 @@ __global__ __launch_bounds__(kThreads) void int8_quant_tensor_kernel(
 // wavefronts); its max is an xor-shuffle over the group.  The trip loop is
 // uniform over the workgroup, and a group lies entirely inside or outside
 // the tensor, so the shuffles of a group inside it only read lanes of the
-// same group (a group outside it reads copies of the last piece and stores
-// nothing).
+// same group.  A group outside it loads the tensor's last block (lane j of
+// the group its piece j), so it derives that block's scale and codes and
+// stores them again, unchanged, in place: no branch surrounds a store, which
+// would make the compiler wait for every load in flight at its join (cold,
+// [4096, 4096] at B = 128: 12.80 -> 11.70 us; the same change took the
+// per-tensor codes 16.1 -> 15.8 us and the decompressions 9.14 -> 8.55 and
+// 8.87 -> 8.42 us).
 template <int G>
 __global__ __launch_bounds__(kThreads) void int8_quant_block_kernel(
     const uint4* __restrict__ x, int64_t n16, float* __restrict__ scale, uint2* __restrict__ q) {
@@ -1939,21 +1944,20 @@ __global__ __launch_bounds__(kThreads) void int8_quant_block_kernel(
 #pragma unroll
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
-      v[u] = x[i < n16 ? i : n16 - 1];      // branch-free: past the end, a copy of the last piece
+      v[u] = x[i < n16 ? i : n16 - G + lane % G];      // past the end: the last block again
     }
     all_loads_issued();
 #pragma unroll
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
+      const int64_t ic = i < n16 ? i : n16 - G + lane % G;
       unsigned m = bf16x8_absmax_bits(v[u]);
 #pragma unroll
       for (int o = 1; o < G; o <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), o)));
       const float s = int8_scale_of(__uint_as_float(m << 16));
       const uint2 c = int8_codes_piece(v[u], s);
-      if (i < n16) {
-        store8<TACO_NT_CODE_STORES != 0>(&q[i], c);
-        if (lane % G == 0) scale[i / G] = s;
-      }
+      store8<TACO_NT_CODE_STORES != 0>(&q[ic], c);
+      scale[ic / G] = s;                    // the group's lanes store the same value
     }
   }
 }
@@ -1982,7 +1986,7 @@ __global__ __launch_bounds__(kThreads) void int8_dequant_kernel(
     for (int u = 0; u < kInt8Unroll; ++u) {
       const int64_t i = base + u * kThreads + threadIdx.x;
       const uint4 o = G == 0 ? bf16_piece_from_int8(c[u], s0, r0) : bf16_piece_from_int8(c[u], sk[u], 1.0f / sk[u]);
-      if (i < n16) store16<TACO_NT_OUT_STORES != 0>(&out[i], o);
+      store16<TACO_NT_OUT_STORES != 0>(&out[i < n16 ? i : n16 - 1], o);   // past the end: the last piece again
     }
   }
 }
